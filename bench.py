@@ -1,0 +1,263 @@
+"""Benchmark of one decode step of paged attention on one MI355X.
+
+A step is the whole hot path over one batch: append each sequence's newest K/V row
+(pkv_kv_append), then paged decode attention over every cached token
+(pkv_paged_decode_attn: the decode kernel and, for split contexts, the partition merge).
+Inputs are seeded synthetic tensors already resident in HBM when timing starts.
+
+Prints one JSON line.  `value` is KV GB/s for the whole step (algorithmic KV bytes read
+per step / step time); decode tokens/s is reported beside it.  `roofline` covers the
+attention call (decode + merge kernels of one pkv_paged_decode_attn call), timed with HIP
+events on the stream the library launches on.  `cpu_baseline` is the fp64 oracle timed
+on a bounded sample of the same workload on this host.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--flush]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attn: KV GB/s read & % of MI355X HBM peak; decode tokens/s"
+HBM_PEAK_GBS = 8000.0                       # MI355X HBM3E, 8 TB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["paged_kv_cache_288_amd/csrc/gqa_decode.hip",
+                  "paged_kv_cache_288_amd/csrc/pkv_device.hpp"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kv_bytes(w):
+    """Algorithmic KV bytes one decode call reads: every cached token's K and V row once
+    (the latent row once for MLA)."""
+    if w.kind == "mla":
+        per_token = w.d * w.elem_bytes
+    else:
+        per_token = 2 * w.Hkv * w.d * w.elem_bytes
+    return int(w.context_lens.astype(np.int64).sum()) * per_token
+
+
+def traffic_for(workload_name):
+    """Measured HBM bytes per call from committed counter runs, if they were taken on
+    the current kernel source; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload_name)
+    if not e or e.get("kernel_hash") != kernel_hash():
+        return None
+    return e.get("bytes_per_call")
+
+
+def cpu_baseline(w, target_s=15.0):
+    """Time the fp64 oracle on the first sequences of the workload (one thread)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:
+        limiter = None
+    order = list(range(w.B))
+    done, tokens, t_total = 0, 0, 0.0
+    while done < len(order) and t_total < target_s:
+        b = order[done]
+        L = int(w.context_lens[b])
+        n = -(-L // w.bs)
+        ids = w.block_table[b, :n]
+        t0 = time.perf_counter()
+        q = oracle.bf16_bits_to_f64(w.q[b:b + 1])
+        table = np.arange(n)[None, :]
+        if w.kind == "mla":
+            kv = oracle.bf16_bits_to_f64(w.k_pool[ids])
+            oracle.mla_decode_attention(q, kv, table, w.context_lens[b:b + 1], w.scale, w.d_v)
+        else:
+            K = oracle.decode_kv_bits(w.k_pool[ids], w.kv_dtype, w.k_scale)
+            V = oracle.decode_kv_bits(w.v_pool[ids], w.kv_dtype, w.v_scale)
+            oracle.paged_decode_attention(q, K, V, table, w.context_lens[b:b + 1], w.scale)
+        t_total += time.perf_counter() - t0
+        tokens += L
+        done += 1
+    per_token = kv_bytes(w) / int(w.context_lens.astype(np.int64).sum())
+    if limiter is not None:
+        limiter.unregister()
+    return {
+        "value": round(tokens * per_token / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"first {done} of {w.B} sequences ({tokens} cached tokens, all {w.Hq} "
+                  f"query heads), gather + fp64 attention, {t_total:.1f} s",
+        "decode_tokens_per_s": round(done / t_total, 4),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gqa70b")
+    ap.add_argument("--partition", type=int, default=None)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--flush", action="store_true",
+                    help="write 512 MiB of scratch before every step (outside the call's events)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (to scale memory counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the decode path "
+                          "has no multi-GPU mode (see DESIGN.md, sharding)"}))
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_288_amd as pkv
+    from paged_kv_cache_288_amd.workloads import make_workload
+
+    if not os.path.exists(pkv.library_path()):
+        from paged_kv_cache_288_amd import build as _b
+        _b.build(verbose=False)
+    pkv.load_library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+
+    t0 = time.time()
+    w = make_workload(args.workload)
+    log(f"workload {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} d={w.d} bs={w.bs} "
+        f"{w.kv_dtype} sum(L)={int(w.context_lens.sum())} (generated in {time.time() - t0:.1f} s)")
+
+    def put(a):
+        if a is None:
+            return None
+        a = a.view(np.int16) if a.dtype == np.uint16 else a
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    q, kp, vp = put(w.q), put(w.k_pool), put(w.v_pool)
+    bt, cl = put(w.block_table), put(w.context_lens)
+    ks, vs = put(w.k_scale), put(w.v_scale)
+    nk, nv, slots = put(w.new_k), put(w.new_v), put(w.slot_mapping)
+    out = torch.empty((w.B, w.Hq, w.d_v), dtype=torch.float32, device=dev)
+    ps = w.partition_size if args.partition is None else args.partition
+    if w.kind == "mla":
+        nbytes = pkv.mla_workspace_bytes(w.B, w.Hq, w.d_v, w.max_context_len, ps)
+    else:
+        nbytes = pkv.decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, w.max_context_len, ps)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.flush else None
+    torch.cuda.synchronize()
+
+    def attend():
+        if w.kind == "mla":
+            pkv.paged_decode_attn_mla(out, q, kp, bt, cl, w.scale, w.max_context_len, d_v=w.d_v,
+                                      partition_size=ps, workspace=ws)
+        else:
+            pkv.paged_decode_attn(out, q, kp, vp, bt, cl, w.scale, w.max_context_len,
+                                  kv_dtype=w.kv_dtype, k_scale=ks, v_scale=vs,
+                                  partition_size=ps, workspace=ws)
+
+    def step(ev=None):
+        if flush_buf is not None:
+            flush_buf.fill_(1)
+        pkv.kv_append(kp, vp, nk, nv, slots, kv_dtype=w.kv_dtype)
+        if ev is not None:
+            ev[0].record()
+        attend()
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    call_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ms_per_step = total_ms / args.steps
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    kvb = kv_bytes(w)
+    call_avg = float(call_ms.mean())
+    achieved = kvb / (call_avg * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(kvb / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+            "head_dim": w.d, "block_size": w.bs, "kv_dtype": w.kv_dtype,
+            "context_tokens": int(w.context_lens.sum()),
+            "max_context_len": w.max_context_len,
+            "partition_size": int(pkv.decode_partition_size(w.B, w.Hkv, w.max_context_len, ps))
+            if w.kind != "mla" else ps,
+            "kv_bytes_per_step": kvb, "flush_between_steps": bool(args.flush),
+        },
+        "decode_tokens_per_s": round(w.B / (ms_per_step * 1e-3), 1),
+        "hbm_peak_frac_step": round(kvb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_for(w.name),
+            "kernel": "pkv_paged_decode_attn call (gqa_decode_kernel + partition_merge_kernel)"
+            if w.kind != "mla" else "pkv_paged_decode_attn_mla call",
+            "call_ms_avg": round(call_avg, 5),
+            "call_ms_median": round(float(np.median(call_ms)), 5),
+            "call_ms_p90": round(float(np.percentile(call_ms, 90)), 5),
+            "algorithmic_bytes_per_call": kvb,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        log("timing the oracle on a sample (one core)...")
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

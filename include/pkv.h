@@ -1,0 +1,184 @@
+/*
+ * pkv.h — decode attention over a paged KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (pages cited by title and section):
+ *  - "深入LLM推理：从KV Cache到PD分离的Serving全景解析", section "KV Cache：Transformer的循环状态":
+ *    each decode step computes softmax(q K^T * scale) V for one new query token per head
+ *    over every cached position; under GQA a group of query heads shares one K/V head.
+ *  - same page, section "PagedAttention与Cache管理": the cache is a pool of fixed-size
+ *    physical blocks; a per-sequence block table maps logical blocks to physical ones,
+ *    blocks may be shared between sequences, and the kernel has to read this layout.
+ *  - "PD 分离下的 KV Cache", section "先回顾：两个阶段": a decode step adds one token and
+ *    reads the whole cache, so the step is bound by memory bandwidth.
+ *
+ * Conventions for every call:
+ *  - All buffer pointers are DEVICE pointers to row-major, contiguous arrays, 16-byte
+ *    aligned, allocated and owned by the caller.  The library keeps no pointer after
+ *    returning and allocates nothing.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued on it and
+ *    the call returns without synchronising; buffers must stay alive until the stream
+ *    has passed the work.
+ *  - Host-checkable errors (NULL pointers, bad sizes, misalignment, unsupported shapes or
+ *    dtypes, a too-small workspace) are returned before anything is launched.  A failed
+ *    launch returns PKV_ERR_HIP.  No C++ exception crosses this interface.
+ *  - Device-resident indices are the caller's contract, but a bad value never causes an
+ *    out-of-bounds access: block ids outside [0, num_blocks) are not read (their tokens
+ *    are skipped and that sequence's output is then unspecified), context lengths are
+ *    clamped to [0, max_blocks_per_seq * block_size], and append slots outside
+ *    [0, num_blocks * block_size) are skipped.
+ *  - Calls on different streams may overlap; the library has no global mutable state.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+typedef int32_t pkv_status;
+enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = -1,        /* a required pointer is NULL                              */
+  PKV_ERR_SHAPE = -2,       /* a size is non-positive or inconsistent                  */
+  PKV_ERR_DTYPE = -3,       /* unknown element type                                    */
+  PKV_ERR_UNSUPPORTED = -4, /* valid but not implemented (head dim, block size, group) */
+  PKV_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned                        */
+  PKV_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required              */
+  PKV_ERR_HIP = -7          /* the HIP runtime reported an error at launch             */
+};
+
+/* Element types of the KV pools. */
+enum {
+  PKV_BF16 = 1,             /* bfloat16                                                */
+  PKV_FP8_E4M3 = 2          /* OCP FP8 E4M3 ("e4m3fn": bias 7, max 448, no inf), with
+                               one fp32 scale per KV head for K and one for V; the
+                               stored value is e4m3(byte) * scale                      */
+};
+
+/* Returns PKV_ABI_VERSION of the built library. */
+int pkv_abi_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* pkv_status_str(pkv_status s);
+
+/*
+ * pkv_kv_append — write T new tokens' K and V rows into the block pool.
+ *
+ * Cites: "深入LLM推理…" section "PagedAttention与Cache管理" (block + offset addressing) and
+ * section "KV Cache：Transformer的循环状态" (history is never rewritten, only appended).
+ *
+ * For token i with s = slot_mapping[i] in [0, num_blocks*block_size):
+ *     k_pool[s / block_size][h][s % block_size][0:d] = k_new[i][h][0:d]   for every h < Hkv
+ * and the same for V.  Slots < 0 (and out-of-range slots) are skipped.  Every other byte
+ * of the pools is left unchanged; the copy is bit-exact.  Duplicate slots in one call
+ * are a caller error (the surviving row is unspecified).
+ *
+ *   k_pool, v_pool  [num_blocks][Hkv][block_size][d], element type kv_dtype.
+ *                   v_pool may be NULL (then v_new must be NULL too): this is the
+ *                   latent (MLA) cache, written with Hkv = 1.
+ *   k_new, v_new    [T][Hkv][d], same element type as the pools.
+ *   slot_mapping    [T] int64.
+ * Requires d * element_bytes to be a multiple of 16.  T = 0 is a no-op.
+ */
+pkv_status pkv_kv_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                         const int64_t* slot_mapping, int32_t T, int32_t num_blocks,
+                         int32_t Hkv, int32_t d, int32_t block_size, int32_t kv_dtype,
+                         void* stream);
+
+/*
+ * pkv_decode_partition_size — the context partition (tokens) that pkv_paged_decode_attn
+ * will use for these arguments: `partition_size` itself when > 0, otherwise the
+ * library's choice for filling the GPU (a power of two, >= 64).  A result >=
+ * max_context_len means the context is not split.  Negative = error code.
+ */
+int32_t pkv_decode_partition_size(int32_t B, int32_t Hkv, int32_t max_context_len,
+                                  int32_t partition_size);
+
+/*
+ * pkv_decode_workspace_bytes — bytes of workspace pkv_paged_decode_attn needs for these
+ * arguments (0 when the context is not split).  The workspace holds, per (sequence,
+ * query head, partition), the partition's running max, sum and unnormalised output.
+ */
+size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d_v,
+                                  int32_t max_context_len, int32_t partition_size);
+
+/*
+ * pkv_paged_decode_attn — one decode step of GQA/MQA/MHA attention over the paged cache.
+ *
+ * Cites: "深入LLM推理…" section "KV Cache：Transformer的循环状态" (softmax(q K^T / sqrt d) V,
+ * GQA head sharing) and "PagedAttention与Cache管理" (block table).  Long contexts are
+ * split into partitions whose online-softmax partials are merged afterwards ("GPU推理深度
+ * 拆解：KV Cache视角", sections "长上下文优化" and "算子优化要点").
+ *
+ * For sequence b with L = context_lens[b] and query head h (KV head g = h / (Hq/Hkv)):
+ *     token t (0 <= t < L) lives at block block_table[b][t / block_size], offset
+ *     t % block_size;  s_t = scale * k_scale[g] * dot(q[b][h], K_t)
+ *     out[b][h] = v_scale[g] * sum_t softmax(s)_t V_t        (out = 0 when L = 0)
+ * k_scale / v_scale are taken as 1 for bf16 pools.
+ *
+ *   out          [B][Hq][d] float32 (written)
+ *   q            [B][Hq][d] bfloat16
+ *   k_pool       [num_blocks][Hkv][block_size][d], kv_dtype
+ *   v_pool       [num_blocks][Hkv][block_size][d], kv_dtype
+ *   k_scale, v_scale  [Hkv] float32 for PKV_FP8_E4M3, ignored (may be NULL) for bf16
+ *   block_table  [B][max_blocks_per_seq] int32 (entries past a sequence's end unused)
+ *   context_lens [B] int32
+ *   max_context_len   host-side upper bound of context_lens (sizes the grid)
+ *   partition_size    tokens per partition, a multiple of 16, or 0 for the library's
+ *                     choice (see pkv_decode_partition_size)
+ *   workspace, workspace_bytes  >= pkv_decode_workspace_bytes(...) when the context is
+ *                     split; may be NULL/0 otherwise.
+ * Supported: d = 128 with bf16 or FP8 pools, d = 64 with bf16 pools; block_size a
+ * multiple of 16 (16, 32, 64, ...); Hq / Hkv in {1, 2, 4, 8}.  Other shapes return
+ * PKV_ERR_UNSUPPORTED.  q and out must not alias the pools.
+ */
+pkv_status pkv_paged_decode_attn(float* out, const void* q, const void* k_pool,
+                                 const void* v_pool, const float* k_scale, const float* v_scale,
+                                 const int32_t* block_table, const int32_t* context_lens,
+                                 int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                                 int32_t block_size, int32_t num_blocks,
+                                 int32_t max_blocks_per_seq, int32_t max_context_len,
+                                 float scale, int32_t kv_dtype, int32_t partition_size,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_mla_workspace_bytes — workspace bytes for pkv_paged_decode_attn_mla with these
+ * arguments (0 when the context is not split).
+ */
+size_t pkv_mla_workspace_bytes(int32_t B, int32_t Hq, int32_t d_v, int32_t max_context_len,
+                               int32_t partition_size);
+
+/*
+ * pkv_paged_decode_attn_mla — decode attention over a latent (MLA) cache.
+ *
+ * Cites: "深入LLM推理…" section "KV Cache：Transformer的循环状态" and "GPU推理深度拆解：KV Cache
+ * 视角" section "KV Cache 大小与分配演进": one cached latent row per token (512 latent + 64
+ * RoPE dims) serves every query head.  Reading: the key is the whole latent row and the
+ * value its first d_v dims (MQA over the latent).
+ *
+ *     s_t = scale * dot(q[b][h][0:d_qk], C_t[0:d_qk]);  out[b][h] = sum_t softmax(s)_t C_t[0:d_v]
+ *
+ *   out      [B][Hq][d_v] float32;  q [B][Hq][d_qk] bfloat16
+ *   kv_pool  [num_blocks][block_size][d_qk] bfloat16
+ *   block_table, context_lens, max_context_len, partition_size, workspace: as above
+ *   (partition_size a multiple of block_size, or 0 for the library's choice).
+ * Supported: d_qk = 576, d_v = 512, block_size = 64, Hq a multiple of 16 (<= 128).
+ */
+pkv_status pkv_paged_decode_attn_mla(float* out, const void* q, const void* kv_pool,
+                                     const int32_t* block_table, const int32_t* context_lens,
+                                     int32_t B, int32_t Hq, int32_t d_qk, int32_t d_v,
+                                     int32_t block_size, int32_t num_blocks,
+                                     int32_t max_blocks_per_seq, int32_t max_context_len,
+                                     float scale, int32_t partition_size, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

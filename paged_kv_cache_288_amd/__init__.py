@@ -1,0 +1,180 @@
+"""Paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over the C-ABI library ``libpkv.so`` (declared in
+``include/pkv.h``).  It only marshals arguments: tensor data pointers, sizes and
+the current HIP stream go to the library, whose HIP kernels do every step of
+the computation.  PyTorch supplies device memory and streams.  There is no
+fallback: if the library is missing or a call fails, an exception is raised.
+"""
+
+import ctypes
+import os
+
+__all__ = [
+    "PKV_BF16", "PKV_FP8_E4M3", "PkvError", "library_path", "load_library",
+    "abi_version", "kv_append", "decode_partition_size", "decode_workspace_bytes",
+    "paged_decode_attn", "mla_workspace_bytes", "paged_decode_attn_mla",
+]
+
+PKV_BF16 = 1
+PKV_FP8_E4M3 = 2
+_DTYPES = {"bf16": PKV_BF16, "fp8": PKV_FP8_E4M3}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+_c_int32, _c_size, _p = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+
+# (name, restype, argtypes), in the order of include/pkv.h
+_SIGNATURES = [
+    ("pkv_abi_version", ctypes.c_int, []),
+    ("pkv_status_str", ctypes.c_char_p, [_c_int32]),
+    ("pkv_kv_append", _c_int32, [_p, _p, _p, _p, _p, _c_int32, _c_int32, _c_int32, _c_int32,
+                                 _c_int32, _c_int32, _p]),
+    ("pkv_decode_partition_size", _c_int32, [_c_int32, _c_int32, _c_int32, _c_int32]),
+    ("pkv_decode_workspace_bytes", _c_size, [_c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+                                             _c_int32]),
+    ("pkv_paged_decode_attn", _c_int32, [_p, _p, _p, _p, _p, _p, _p, _p, _c_int32, _c_int32,
+                                         _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+                                         _c_int32, ctypes.c_float, _c_int32, _c_int32, _p,
+                                         _c_size, _p]),
+    ("pkv_mla_workspace_bytes", _c_size, [_c_int32, _c_int32, _c_int32, _c_int32, _c_int32]),
+    ("pkv_paged_decode_attn_mla", _c_int32, [_p, _p, _p, _p, _p, _c_int32, _c_int32, _c_int32,
+                                             _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+                                             ctypes.c_float, _c_int32, _p, _c_size, _p]),
+]
+EXPORTED = [name for name, _, _ in _SIGNATURES]
+
+
+class PkvError(RuntimeError):
+    def __init__(self, fn, status, text):
+        super().__init__(f"{fn} failed with status {status}: {text}")
+        self.status = status
+
+
+def library_path():
+    return os.path.join(_HERE, "libpkv.so")
+
+
+def load_library():
+    """Load libpkv.so (built in-tree by ``python -m paged_kv_cache_288_amd.build``)."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run `python -m paged_kv_cache_288_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, res, args in _SIGNATURES:
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def _check(fn, status):
+    if status != 0:
+        raise PkvError(fn, status, load_library().pkv_status_str(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(kv_dtype):
+    if kv_dtype not in _DTYPES:
+        raise ValueError(f"kv_dtype must be one of {sorted(_DTYPES)}")
+    return _DTYPES[kv_dtype]
+
+
+def abi_version():
+    return load_library().pkv_abi_version()
+
+
+def kv_append(k_pool, v_pool, k_new, v_new, slot_mapping, kv_dtype="bf16"):
+    """Scatter new rows into the pool in place (pkv_kv_append).
+
+    k_pool/v_pool [num_blocks, Hkv, block_size, d] (v_pool None for an MLA latent pool
+    [num_blocks, block_size, d]), k_new/v_new [T, Hkv, d], slot_mapping [T] int64.
+    Tensors hold the raw element bits (bf16 as torch.bfloat16/int16/uint16, FP8 as uint8
+    or torch.float8_e4m3fn) on the current device.
+    """
+    mla = v_pool is None
+    if mla:
+        num_blocks, bs, d = k_pool.shape
+        Hkv = 1
+    else:
+        num_blocks, Hkv, bs, d = k_pool.shape
+    T = slot_mapping.shape[0]
+    st = load_library().pkv_kv_append(
+        _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), T,
+        num_blocks, Hkv, d, bs, _dtype_code(kv_dtype), _stream(k_pool.device))
+    _check("pkv_kv_append", st)
+
+
+def decode_partition_size(B, Hkv, max_context_len, partition_size=0):
+    return load_library().pkv_decode_partition_size(B, Hkv, max_context_len, partition_size)
+
+
+def decode_workspace_bytes(B, Hq, Hkv, d, max_context_len, partition_size=0):
+    return load_library().pkv_decode_workspace_bytes(B, Hq, Hkv, d, max_context_len, partition_size)
+
+
+def _workspace(nbytes, device, workspace):
+    import torch
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def paged_decode_attn(out, q, k_pool, v_pool, block_table, context_lens, scale, max_context_len,
+                      kv_dtype="bf16", k_scale=None, v_scale=None, partition_size=0,
+                      workspace=None):
+    """out[B, Hq, d] (fp32) = paged decode attention (pkv_paged_decode_attn).
+
+    q [B, Hq, d] bf16; pools [num_blocks, Hkv, block_size, d]; block_table
+    [B, max_blocks] int32; context_lens [B] int32; k_scale/v_scale [Hkv] fp32 for FP8.
+    The workspace (device bytes) is allocated here with torch when not given.
+    """
+    B, Hq, d = q.shape
+    num_blocks, Hkv, bs, _ = k_pool.shape
+    lib = load_library()
+    nbytes = lib.pkv_decode_workspace_bytes(B, Hq, Hkv, d, max_context_len, partition_size)
+    workspace, wsize = _workspace(nbytes, q.device, workspace)
+    st = lib.pkv_paged_decode_attn(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_table), _ptr(context_lens), B, Hq, Hkv, d, bs, num_blocks,
+        block_table.shape[1], max_context_len, float(scale), _dtype_code(kv_dtype),
+        partition_size, _ptr(workspace), wsize, _stream(q.device))
+    _check("pkv_paged_decode_attn", st)
+    return out
+
+
+def mla_workspace_bytes(B, Hq, d_v, max_context_len, partition_size=0):
+    return load_library().pkv_mla_workspace_bytes(B, Hq, d_v, max_context_len, partition_size)
+
+
+def paged_decode_attn_mla(out, q, kv_pool, block_table, context_lens, scale, max_context_len,
+                          d_v=512, partition_size=0, workspace=None):
+    """out[B, Hq, d_v] (fp32) = latent decode attention (pkv_paged_decode_attn_mla).
+
+    q [B, Hq, d_qk] bf16; kv_pool [num_blocks, block_size, d_qk] bf16.
+    """
+    B, Hq, d_qk = q.shape
+    num_blocks, bs, _ = kv_pool.shape
+    lib = load_library()
+    nbytes = lib.pkv_mla_workspace_bytes(B, Hq, d_v, max_context_len, partition_size)
+    workspace, wsize = _workspace(nbytes, q.device, workspace)
+    st = lib.pkv_paged_decode_attn_mla(
+        _ptr(out), _ptr(q), _ptr(kv_pool), _ptr(block_table), _ptr(context_lens), B, Hq, d_qk,
+        d_v, bs, num_blocks, block_table.shape[1], max_context_len, float(scale),
+        partition_size, _ptr(workspace), wsize, _stream(q.device))
+    _check("pkv_paged_decode_attn_mla", st)
+    return out

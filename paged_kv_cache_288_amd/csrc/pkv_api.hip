@@ -1,0 +1,213 @@
+// C-ABI of the paged decode-attention library: argument validation, partition choice,
+// workspace sizing and dispatch to the kernel launchers.  Validation touches no HIP API,
+// so every error return happens before anything is enqueued.
+#include <stdint.h>
+
+#include "../../include/pkv.h"
+#include "pkv_launch.hpp"
+
+namespace {
+
+constexpr int kMaxPartitionTokens = 4096;  // 64 tiles of 16 tokens per wave, 4 waves
+constexpr int kGridYZMax = 65535;
+constexpr long long kTargetWorkgroups = 2048;  // ~8 workgroups per CU on 256 CUs
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int elem_bytes(int32_t dtype) {
+  return dtype == PKV_BF16 ? 2 : (dtype == PKV_FP8_E4M3 ? 1 : 0);
+}
+
+int32_t auto_partition(int32_t B, int32_t heads, int32_t max_ctx) {
+  int32_t ps = 512;
+  while (ps > 64) {
+    const long long parts = (max_ctx + ps - 1) / ps;
+    if ((long long)B * heads * (parts > 0 ? parts : 1) >= kTargetWorkgroups) break;
+    ps /= 2;
+  }
+  return ps;
+}
+
+int32_t num_parts(int32_t max_ctx, int32_t ps) {
+  const int32_t p = (max_ctx + ps - 1) / ps;
+  return p < 1 ? 1 : p;
+}
+
+// Workspace layout, shared by both decode entry points: m [R], l [R], o [R][d_v] (fp32),
+// R = B * Hq * P, each section 256-byte aligned.
+size_t ws_bytes(int32_t B, int32_t Hq, int32_t d_v, int32_t P) {
+  if (P <= 1) return 0;
+  const size_t rows = (size_t)B * Hq * P;
+  return 2 * round256(rows * sizeof(float)) + round256(rows * d_v * sizeof(float));
+}
+
+void ws_split(void* ws, int32_t B, int32_t Hq, int32_t P, float** m, float** l, float** o) {
+  const size_t rows = (size_t)B * Hq * P;
+  char* base = (char*)ws;
+  *m = (float*)base;
+  *l = (float*)(base + round256(rows * sizeof(float)));
+  *o = (float*)(base + 2 * round256(rows * sizeof(float)));
+}
+
+pkv_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return PKV_OK;
+  if (e == hipErrorNotSupported) return PKV_ERR_UNSUPPORTED;
+  return PKV_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+const char* pkv_status_str(pkv_status s) {
+  switch (s) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "a size is non-positive or inconsistent";
+    case PKV_ERR_DTYPE: return "unknown element type";
+    case PKV_ERR_UNSUPPORTED: return "shape or type combination not supported";
+    case PKV_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+pkv_status pkv_kv_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                         const int64_t* slot_mapping, int32_t T, int32_t num_blocks,
+                         int32_t Hkv, int32_t d, int32_t block_size, int32_t kv_dtype,
+                         void* stream) {
+  if (T < 0 || num_blocks <= 0 || Hkv <= 0 || d <= 0 || block_size <= 0) return PKV_ERR_SHAPE;
+  const int es = elem_bytes(kv_dtype);
+  if (!es) return PKV_ERR_DTYPE;
+  if (T == 0) return PKV_OK;
+  if (!k_pool || !k_new || !slot_mapping) return PKV_ERR_NULL;
+  if ((v_pool == nullptr) != (v_new == nullptr)) return PKV_ERR_NULL;
+  if (((long long)d * es) % 16) return PKV_ERR_UNSUPPORTED;
+  if (!aligned16(k_pool) || !aligned16(k_new) || (v_pool && (!aligned16(v_pool) || !aligned16(v_new))) ||
+      ((uintptr_t)slot_mapping & 7u))
+    return PKV_ERR_ALIGN;
+  pkv::AppendArgs a{k_pool, v_pool, k_new, v_new, slot_mapping, T, num_blocks, Hkv, block_size,
+                    d * es};
+  return hip_status(pkv::launch_kv_append(a, (hipStream_t)stream));
+}
+
+int32_t pkv_decode_partition_size(int32_t B, int32_t Hkv, int32_t max_context_len,
+                                  int32_t partition_size) {
+  if (B < 0 || Hkv <= 0 || max_context_len < 0) return PKV_ERR_SHAPE;
+  if (partition_size < 0 || partition_size % 16 || partition_size > kMaxPartitionTokens)
+    return PKV_ERR_SHAPE;
+  return partition_size > 0 ? partition_size : auto_partition(B, Hkv, max_context_len);
+}
+
+size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d_v,
+                                  int32_t max_context_len, int32_t partition_size) {
+  const int32_t ps = pkv_decode_partition_size(B, Hkv, max_context_len, partition_size);
+  if (ps <= 0 || Hq <= 0 || d_v <= 0) return 0;
+  return ws_bytes(B, Hq, d_v, num_parts(max_context_len, ps));
+}
+
+pkv_status pkv_paged_decode_attn(float* out, const void* q, const void* k_pool,
+                                 const void* v_pool, const float* k_scale, const float* v_scale,
+                                 const int32_t* block_table, const int32_t* context_lens,
+                                 int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                                 int32_t block_size, int32_t num_blocks,
+                                 int32_t max_blocks_per_seq, int32_t max_context_len,
+                                 float scale, int32_t kv_dtype, int32_t partition_size,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || block_size <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || max_context_len < 0)
+    return PKV_ERR_SHAPE;
+  if (Hq % Hkv) return PKV_ERR_SHAPE;
+  if (!elem_bytes(kv_dtype)) return PKV_ERR_DTYPE;
+  if (B == 0) return PKV_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_table || !context_lens) return PKV_ERR_NULL;
+  const bool fp8 = kv_dtype == PKV_FP8_E4M3;
+  if (fp8 && (!k_scale || !v_scale)) return PKV_ERR_NULL;
+  const int32_t G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PKV_ERR_UNSUPPORTED;
+  if (!((d == 128) || (d == 64 && !fp8))) return PKV_ERR_UNSUPPORTED;
+  if (block_size % 16) return PKV_ERR_UNSUPPORTED;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      !aligned4(block_table) || !aligned4(context_lens) ||
+      (fp8 && (!aligned4(k_scale) || !aligned4(v_scale))))
+    return PKV_ERR_ALIGN;
+  if (B > kGridYZMax) return PKV_ERR_SHAPE;
+  // Grid and workspace follow max_context_len exactly as pkv_decode_workspace_bytes does;
+  // each sequence's own length is clamped to its table inside the kernels.
+  const int32_t ctx = max_context_len;
+  const int32_t ps = pkv_decode_partition_size(B, Hkv, ctx, partition_size);
+  if (ps <= 0) return PKV_ERR_SHAPE;
+  const int32_t P = num_parts(ctx, ps);
+  if (P > kGridYZMax) return PKV_ERR_SHAPE;
+  float *ws_m = nullptr, *ws_l = nullptr, *ws_o = nullptr;
+  if (P > 1) {
+    if (!workspace || workspace_bytes < ws_bytes(B, Hq, d, P)) return PKV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+    ws_split(workspace, B, Hq, P, &ws_m, &ws_l, &ws_o);
+  }
+  pkv::DecodeArgs a{out, (const uint16_t*)q, (const uint8_t*)k_pool, (const uint8_t*)v_pool,
+                    k_scale, v_scale, block_table, context_lens, ws_m, ws_l, ws_o,
+                    B, Hq, Hkv, d, block_size, num_blocks, max_blocks_per_seq, ctx,
+                    ps, P, scale, fp8 ? 1 : 0};
+  hipStream_t s = (hipStream_t)stream;
+  pkv_status st = hip_status(pkv::launch_gqa_decode(a, s));
+  if (st != PKV_OK || P == 1) return st;
+  return hip_status(pkv::launch_partition_merge(ws_m, ws_l, ws_o, context_lens, out, B, Hq, d,
+                                                ps, P, ctx,
+                                                max_blocks_per_seq * block_size, s));
+}
+
+size_t pkv_mla_workspace_bytes(int32_t B, int32_t Hq, int32_t d_v, int32_t max_context_len,
+                               int32_t partition_size) {
+  if (B < 0 || Hq <= 0 || d_v <= 0 || max_context_len < 0 || partition_size < 0) return 0;
+  const int32_t ps = partition_size > 0 ? partition_size : auto_partition(B, 1, max_context_len);
+  return ws_bytes(B, Hq, d_v, num_parts(max_context_len, ps));
+}
+
+pkv_status pkv_paged_decode_attn_mla(float* out, const void* q, const void* kv_pool,
+                                     const int32_t* block_table, const int32_t* context_lens,
+                                     int32_t B, int32_t Hq, int32_t d_qk, int32_t d_v,
+                                     int32_t block_size, int32_t num_blocks,
+                                     int32_t max_blocks_per_seq, int32_t max_context_len,
+                                     float scale, int32_t partition_size, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (B < 0 || Hq <= 0 || d_qk <= 0 || d_v <= 0 || block_size <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || max_context_len < 0 || partition_size < 0)
+    return PKV_ERR_SHAPE;
+  if (d_v > d_qk) return PKV_ERR_SHAPE;
+  if (B == 0) return PKV_OK;
+  if (!out || !q || !kv_pool || !block_table || !context_lens) return PKV_ERR_NULL;
+  if (d_qk != 576 || d_v != 512 || block_size != 64 || Hq % 16 || Hq > 128)
+    return PKV_ERR_UNSUPPORTED;
+  if (partition_size % block_size) return PKV_ERR_SHAPE;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(kv_pool) || !aligned4(block_table) ||
+      !aligned4(context_lens))
+    return PKV_ERR_ALIGN;
+  if (B > kGridYZMax) return PKV_ERR_SHAPE;
+  const int32_t ctx = max_context_len;
+  const int32_t ps = partition_size > 0 ? partition_size : auto_partition(B, 1, ctx);
+  const int32_t P = num_parts(ctx, ps);
+  if (P > kGridYZMax) return PKV_ERR_SHAPE;
+  float *ws_m = nullptr, *ws_l = nullptr, *ws_o = nullptr;
+  if (P > 1) {
+    if (!workspace || workspace_bytes < ws_bytes(B, Hq, d_v, P)) return PKV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+    ws_split(workspace, B, Hq, P, &ws_m, &ws_l, &ws_o);
+  }
+  pkv::MlaArgs a{out, (const uint16_t*)q, (const uint16_t*)kv_pool, block_table, context_lens,
+                 ws_m, ws_l, ws_o, B, Hq, d_qk, d_v, block_size, num_blocks, max_blocks_per_seq,
+                 ctx, ps, P, scale};
+  hipStream_t s = (hipStream_t)stream;
+  pkv_status st = hip_status(pkv::launch_mla_decode(a, s));
+  if (st != PKV_OK || P == 1) return st;
+  return hip_status(pkv::launch_partition_merge(ws_m, ws_l, ws_o, context_lens, out, B, Hq, d_v,
+                                                ps, P, ctx,
+                                                max_blocks_per_seq * block_size, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// Device helpers for the gfx950 (CDNA4) kernels: wave64 cross-lane moves, bf16 pairs
+// for v_dot2c_f32_bf16, FP8 E4M3 -> bf16 conversion.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- DPP controls (gfx9 encoding)
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror: lane i <- lane 7-i within 8 lanes
+constexpr int kDppRowRor8 = 0x128;     // row_ror:8: lane i <- lane (i+8)%16 within a row
+constexpr int kDppRowNewBcast = 0x150; // row_newbcast:n: every lane of a row <- lane n of it
+
+// Every control used here reads a valid lane for every lane, so bound_ctrl never applies;
+// setting it lets the compiler skip initialising the destination.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
+}
+
+// Broadcast lane n (0..15) of each 16-lane row to the whole row.
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) { return dpp<kDppRowNewBcast + N>(x); }
+template <int N>
+__device__ __forceinline__ uint32_t row_bcast_u(uint32_t x) { return dpp_u<kDppRowNewBcast + N>(x); }
+
+// Exchange between row pairs (0<->1, 2<->3): returns {value of the even row, value of the
+// odd row} of each pair, in every lane of both rows.
+__device__ __forceinline__ void rows_pair16(float x, float& even, float& odd) {
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  even = __builtin_bit_cast(float, (uint32_t)r[0]);
+  odd = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+// Exchange between wave halves: returns {lower-half value, upper-half value} in every lane.
+__device__ __forceinline__ void halves_pair32(float x, float& lo, float& hi) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  lo = __builtin_bit_cast(float, (uint32_t)r[0]);
+  hi = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// ---------------------------------------------------------------- arithmetic helpers
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+// (lo, hi) -> packed bf16 pair, round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+// Two FP8 E4M3 bytes (low or high 16 bits of x) -> two bf16 (exact).
+template <bool HIGH>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t x) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, HIGH));
+}
+__device__ __forceinline__ uint32_t byte_perm(uint32_t s0, uint32_t s1, uint32_t sel) {
+  return __builtin_amdgcn_perm(s0, s1, sel);
+}
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;   // (1.0, 1.0) in bf16
+
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+}  // namespace pkv

@@ -1,0 +1,61 @@
+// Internal host-side launchers; each kernel translation unit defines its own.  Arguments
+// are validated by the C-ABI layer (pkv_api.hip) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct AppendArgs {
+  void* k_pool;
+  void* v_pool;
+  const void* k_new;
+  const void* v_new;
+  const int64_t* slots;
+  int32_t T, num_blocks, Hkv, block_size;
+  int32_t row_bytes;  // d * element bytes
+};
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
+
+struct DecodeArgs {
+  float* out;
+  const uint16_t* q;
+  const uint8_t* k_pool;
+  const uint8_t* v_pool;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  float* ws_m;  // [B][Hq][P]
+  float* ws_l;  // [B][Hq][P]
+  float* ws_o;  // [B][Hq][P][d]
+  int32_t B, Hq, Hkv, d, block_size, num_blocks, max_blocks, max_context_len;
+  int32_t partition, num_partitions;  // num_partitions == 1: no split, out written directly
+  float scale;
+  int32_t fp8;
+};
+hipError_t launch_gqa_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_partition_merge(const float* ws_m, const float* ws_l, const float* ws_o,
+                                  const int32_t* context_lens, float* out, int32_t B,
+                                  int32_t Hq, int32_t d, int32_t partition,
+                                  int32_t num_partitions, int32_t max_context_len,
+                                  int32_t max_ctx_clamp, hipStream_t s);
+
+struct MlaArgs {
+  float* out;
+  const uint16_t* q;
+  const uint16_t* kv_pool;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  float* ws_m;
+  float* ws_l;
+  float* ws_o;
+  int32_t B, Hq, d_qk, d_v, block_size, num_blocks, max_blocks, max_context_len;
+  int32_t partition, num_partitions;
+  float scale;
+};
+hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t s);
+
+}  // namespace pkv

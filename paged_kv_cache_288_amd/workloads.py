@@ -142,9 +142,9 @@ def _lengths(rng, spec, B):
     raise ValueError(kind)
 
 
-def make_workload(name, seed=0, B=None, lens=None, pool=None):
-    """Build a workload by name (or alias); ``B``/``lens``/``pool`` override the
-    spec to make reduced-size variants of the same structure."""
+def make_workload(name, seed=0, B=None, lens=None, pool=None, heads=None):
+    """Build a workload by name (or alias); ``B``/``lens``/``pool``/``heads`` (a pair
+    Hq, Hkv) override the spec to make reduced-size variants of the same structure."""
     name = ALIASES.get(name, name)
     index, spec = SPECS[name]
     spec = dict(spec)
@@ -154,6 +154,8 @@ def make_workload(name, seed=0, B=None, lens=None, pool=None):
         spec["lens"] = lens
     if pool is not None:
         spec["pool"] = pool
+    if heads is not None:
+        spec["Hq"], spec["Hkv"] = heads
     rng = np.random.default_rng([288, index, seed])
     kind = spec["kind"]
     B, Hq, Hkv, d, bs = spec["B"], spec["Hq"], spec["Hkv"], spec["d"], spec["bs"]

@@ -1,0 +1,140 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the header
+declares, and rejects bad arguments on the host before anything is enqueued."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_288_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pkv.library_path()):
+        from paged_kv_cache_288_amd import build
+        build.build(verbose=False)
+    return pkv.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported(lib):
+    declared = header_functions()
+    assert declared, "no declarations found"
+    assert sorted(declared) == sorted(pkv.EXPORTED), "binding signatures out of sync with pkv.h"
+    for name in declared:
+        assert hasattr(lib, name), f"{name} not exported"
+    nm = os.popen(f"nm -D --defined-only {pkv.library_path()}").read()
+    for name in declared:
+        assert re.search(rf"\bT {name}\b", nm), f"{name} is not a defined text symbol"
+
+
+def test_abi_version_and_status_strings(lib):
+    ver = re.search(r"#define PKV_ABI_VERSION (\d+)", open(HEADER).read()).group(1)
+    assert lib.pkv_abi_version() == int(ver)
+    for code in range(-7, 1):
+        assert lib.pkv_status_str(code)
+    assert lib.pkv_status_str(0) == b"ok"
+
+
+FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: every call below returns early
+MIS = ctypes.c_void_p(0x1004)       # misaligned
+
+
+def decode(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, ks=None, vs=None, bt=FAKE, cl=FAKE, B=2, Hq=8,
+             Hkv=1, d=128, bs=16, nb=10, mb=4, ctx=64, scale=0.1, dt=pkv.PKV_BF16, ps=0,
+             ws=None, wsb=0)
+    a.update(kw)
+    return lib.pkv_paged_decode_attn(a["out"], a["q"], a["k"], a["v"], a["ks"], a["vs"], a["bt"],
+                                     a["cl"], a["B"], a["Hq"], a["Hkv"], a["d"], a["bs"], a["nb"],
+                                     a["mb"], a["ctx"], a["scale"], a["dt"], a["ps"], a["ws"],
+                                     a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=0), -2), (dict(Hq=12, Hkv=8), -2), (dict(d=-1), -2), (dict(ctx=-5), -2),
+    (dict(dt=7), -3),
+    (dict(out=None), -1), (dict(bt=None), -1), (dict(dt=pkv.PKV_FP8_E4M3), -1),
+    (dict(Hq=16, Hkv=1), -4), (dict(Hq=3, Hkv=1), -4), (dict(d=96), -4), (dict(bs=8), -4),
+    (dict(d=64, dt=pkv.PKV_FP8_E4M3, ks=FAKE, vs=FAKE), -4),
+    (dict(q=MIS), -5), (dict(k=MIS), -5),
+    (dict(ctx=8192, ps=512, mb=512), -6),                       # split needs a workspace
+    (dict(ctx=8192, ps=512, mb=512, ws=FAKE, wsb=100), -6),     # too small
+    (dict(ps=24), -2), (dict(ps=8192), -2),
+])
+def test_decode_rejects_bad_arguments_before_launch(lib, kw, code):
+    assert decode(lib, **kw) == code
+
+
+def test_decode_empty_batch_is_a_noop(lib):
+    assert decode(lib, B=0, out=None, q=None) == 0
+
+
+def test_append_rejects_bad_arguments_before_launch(lib):
+    f = lib.pkv_kv_append
+    ok = (FAKE, FAKE, FAKE, FAKE, FAKE, 4, 10, 8, 128, 16, pkv.PKV_BF16, None)
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a5=-1) == -2
+    assert call(a10=9) == -3
+    assert call(a0=None) == -1
+    assert call(a1=None) == -1           # v_pool without v_new
+    assert call(a8=7) == -4              # 7 * 2 bytes is not a multiple of 16
+    assert call(a2=MIS) == -5
+    assert call(a5=0, a0=None, a2=None) == 0   # T = 0 is a no-op
+
+
+def test_partition_and_workspace_sizing(lib):
+    # explicit partition: 32768 tokens / 512 = 64 partitions of [m, l, o[128]] per head
+    assert lib.pkv_decode_partition_size(4, 8, 32768, 512) == 512
+    rows = 4 * 64 * 64
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert lib.pkv_decode_workspace_bytes(4, 64, 8, 128, 32768, 512) == 2 * r256(rows * 4) + r256(rows * 128 * 4)
+    # no split needed -> no workspace
+    assert lib.pkv_decode_workspace_bytes(4, 64, 8, 128, 512, 512) == 0
+    # automatic choice fills the GPU: a power of two in [64, 512]
+    for B, H, ctx in [(64, 8, 8192), (2, 1, 256), (1, 8, 32768), (128, 8, 6144)]:
+        ps = lib.pkv_decode_partition_size(B, H, ctx, 0)
+        assert ps in (64, 128, 256, 512)
+    assert lib.pkv_decode_partition_size(64, 8, 8192, 0) == 512
+    assert lib.pkv_decode_partition_size(2, 1, 256, 0) == 64
+    assert lib.pkv_decode_partition_size(1, 8, 100, 20) < 0
+
+
+def test_mla_rejects_bad_arguments_before_launch(lib):
+    f = lib.pkv_paged_decode_attn_mla
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, 2, 128, 576, 512, 64, 10, 4, 200, 0.1, 0, None, 0, None]
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a6=0) == -2
+    assert call(a8=600) == -2            # d_v > d_qk
+    assert call(a0=None) == -1
+    assert call(a7=512, a8=256) == -4
+    assert call(a9=32) == -4
+    assert call(a6=100) == -4
+    assert call(a14=96) == -2            # partition not a multiple of the block size
+    assert call(a1=MIS) == -5
+    assert call(a12=8192, a14=64) == -6  # split without a workspace
+
+
+def test_binding_refuses_to_run_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(pkv, "_LIB", None)
+    monkeypatch.setattr(pkv, "library_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        pkv.load_library()

@@ -1,0 +1,195 @@
+"""GPU parity of pkv_paged_decode_attn (through the C-ABI) against the fp64 oracle.
+
+Reduced-size variants of every workload (several seeds, spanning many tiles, several
+partitions and ragged tails) are compared element by element on all outputs; the
+full-size workloads, run with the same launch configuration the benchmark times, are
+compared on a sample of sequences the oracle computes one by one.  Properties the
+mathematics fixes (block permutation, a single-token context, linearity in V, grouped
+heads versus replicated K/V, NaN poison outside the context) are checked on the GPU
+output itself."""
+
+import numpy as np
+import pytest
+
+from gpu_common import (TOL, assert_close, gpu_decode, log, make_workload, oracle_decode,
+                        to_device, torch_cuda)
+
+pytestmark = pytest.mark.gpu
+
+REDUCED = {
+    "tiny": {},
+    "gqa70b": dict(B=6, lens=("uniform", 100, 1500)),
+    "splitk": dict(B=2, lens=("fixed", [3000, 3000])),
+    "fp8prefix": dict(B=6, lens=("prefix", 256, 17, 300)),
+}
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_decode_matches_oracle_reduced(name, seed):
+    torch = torch_cuda()
+    w = make_workload(name, seed=seed, **REDUCED[name])
+    log(f"[decode] {w.name} seed={seed} B={w.B} lens={w.context_lens.tolist()[:8]}")
+    got = gpu_decode(torch, w)
+    assert_close(got, oracle_decode(w), w.kv_dtype, f"{name}/{seed}")
+
+
+@pytest.mark.parametrize("ps", [16, 48, 64, 256, 512, 4096])
+def test_decode_every_partition_size(ps):
+    torch = torch_cuda()
+    w = make_workload("gqa70b", seed=5, B=4, lens=("uniform", 1, 2100))
+    log(f"[decode] partition={ps} lens={w.context_lens.tolist()}")
+    got = gpu_decode(torch, w, partition_size=ps)
+    assert_close(got, oracle_decode(w), "bf16", f"partition {ps}")
+
+
+@pytest.mark.parametrize("heads", [(8, 8), (16, 8), (32, 8), (8, 1), (2, 1)])
+@pytest.mark.parametrize("name", ["gqa70b", "tiny"])
+def test_decode_group_sizes(name, heads):
+    torch = torch_cuda()
+    w = make_workload(name, seed=7, B=3, lens=("uniform", 1, 700), heads=heads)
+    log(f"[decode] {name} heads={heads} lens={w.context_lens.tolist()}")
+    assert_close(gpu_decode(torch, w), oracle_decode(w), "bf16", f"{name} heads {heads}")
+
+
+def test_decode_fp8_group_sizes():
+    torch = torch_cuda()
+    for heads in [(8, 8), (16, 8), (64, 8)]:
+        w = make_workload("fp8prefix", seed=3, B=3, lens=("prefix", 64, 1, 500), heads=heads)
+        log(f"[decode] fp8 heads={heads} lens={w.context_lens.tolist()}")
+        assert_close(gpu_decode(torch, w), oracle_decode(w), "fp8", f"fp8 heads {heads}")
+
+
+def test_block_size_32_and_64():
+    torch = torch_cuda()
+    for bs in (32, 64):
+        w = make_workload("gqa70b", seed=8, B=3, lens=("uniform", 1, 900))
+        # regroup the same logical history into bigger blocks: a fresh workload of that
+        # block size is simplest, built by re-blocking the pools on the host
+        L = w.context_lens
+        nb = int(sum(-(-int(x) // bs) for x in L)) + 3
+        rng = np.random.default_rng(bs)
+        perm = rng.permutation(nb)
+        kp = np.full((nb, w.Hkv, bs, w.d), 0x7FC0, np.uint16)
+        vp = kp.copy()
+        table = np.full((w.B, -(-int(L.max()) // bs)), -1, np.int32)
+        cur = 0
+        for b in range(w.B):
+            n = -(-int(L[b]) // bs)
+            table[b, :n] = perm[cur:cur + n]
+            cur += n
+            for t in range(int(L[b])):
+                src = w.block_table[b, t // 16], t % 16
+                kp[table[b, t // bs], :, t % bs] = w.k_pool[src[0], :, src[1]]
+                vp[table[b, t // bs], :, t % bs] = w.v_pool[src[0], :, src[1]]
+        ref = oracle_decode(w)
+        w.k_pool, w.v_pool, w.block_table, w.bs = kp, vp, table, bs
+        log(f"[decode] block size {bs}")
+        assert_close(gpu_decode(torch, w), ref, "bf16", f"block size {bs}")
+
+
+@pytest.mark.parametrize("name,nsample", [("gqa70b", 8), ("splitk", 1), ("fp8prefix", 8)])
+def test_decode_full_size_sampled(name, nsample):
+    """Full-size workload, library-chosen (or the workload's) partitioning, as benchmarked."""
+    torch = torch_cuda()
+    w = make_workload(name)
+    log(f"[decode] full size {w.name}: B={w.B} max_ctx={w.max_context_len}")
+    got = gpu_decode(torch, w)
+    rng = np.random.default_rng(123)
+    seqs = sorted(rng.choice(w.B, size=nsample, replace=False).tolist())
+    ref = oracle_decode(w, seqs)
+    assert_close(got[seqs], ref, w.kv_dtype, f"{name} sampled {seqs}")
+    # every output row is finite and a convex combination: bounded by the V range
+    assert np.isfinite(got).all()
+
+
+def test_block_permutation_is_bitwise_invisible():
+    torch = torch_cuda()
+    w = make_workload("gqa70b", seed=11, B=4, lens=("uniform", 30, 1200))
+    base = gpu_decode(torch, w)
+    rng = np.random.default_rng(0)
+    p = rng.permutation(w.num_blocks)
+    kp, vp = np.empty_like(w.k_pool), np.empty_like(w.v_pool)
+    kp[p], vp[p] = w.k_pool, w.v_pool
+    w.k_pool, w.v_pool = kp, vp
+    w.block_table = np.where(w.block_table >= 0, p[np.maximum(w.block_table, 0)], -1).astype(np.int32)
+    assert np.array_equal(gpu_decode(torch, w), base)
+
+
+def test_single_token_context_returns_v_exactly():
+    torch = torch_cuda()
+    for name in ("tiny", "gqa70b", "fp8prefix"):
+        kw = dict(B=3, lens=("fixed", [1, 1, 1])) if name != "fp8prefix" else \
+            dict(B=3, lens=("prefix", 0, 1, 1))
+        w = make_workload(name, seed=2, **kw)
+        got = gpu_decode(torch, w)
+        ref = oracle_decode(w)
+        if w.kv_dtype == "bf16":
+            assert np.array_equal(got.astype(np.float64), ref), name
+        else:
+            assert_close(got, ref, "fp8", name)
+
+
+def test_linearity_in_v_is_exact():
+    torch = torch_cuda()
+    w = make_workload("gqa70b", seed=12, B=3, lens=("uniform", 50, 1500))
+    a = gpu_decode(torch, w)
+    v = w.v_pool.copy()
+    finite = (v & 0x7F80) != 0x7F80
+    exp = (v >> 7) & 0xFF
+    ok = finite & (exp > 0) & (exp < 0xFE)
+    w.v_pool = np.where(ok, v + np.uint16(1 << 7), v).astype(np.uint16)   # x2: exponent + 1
+    b = gpu_decode(torch, w)
+    assert np.array_equal(b, 2 * a)
+
+
+def test_grouped_heads_equal_replicated_kv():
+    torch = torch_cuda()
+    w = make_workload("gqa70b", seed=13, B=3, lens=("uniform", 40, 900))
+    a = gpu_decode(torch, w)
+    w.k_pool = np.repeat(w.k_pool, 8, axis=1)
+    w.v_pool = np.repeat(w.v_pool, 8, axis=1)
+    w.Hkv = 64
+    b = gpu_decode(torch, w)
+    assert_close(a, b.astype(np.float64), "bf16", "GQA vs replicated MHA")
+
+
+def test_poison_outside_context_is_never_used():
+    torch = torch_cuda()
+    w = make_workload("gqa70b", seed=14, B=4, lens=("uniform", 1, 600))
+    poisoned = gpu_decode(torch, w)
+    for pool in (w.k_pool, w.v_pool):
+        pool[pool == 0x7FC0] = 0
+    assert np.array_equal(gpu_decode(torch, w), poisoned)
+
+
+def test_constant_v_returns_the_constant():
+    torch = torch_cuda()
+    w = make_workload("gqa70b", seed=15, B=2, lens=("uniform", 100, 2000))
+    w.v_pool[:] = np.uint16(0x3FC0)          # 1.5
+    got = gpu_decode(torch, w)
+    assert np.abs(got - 1.5).max() <= TOL["bf16"][0] + TOL["bf16"][1] * 1.5
+
+
+def test_empty_sequence_gives_zero():
+    torch = torch_cuda()
+    w = make_workload("gqa70b", seed=16, B=3, lens=("uniform", 100, 1300))
+    w.context_lens[1] = 0
+    for ps in (0, 4096):
+        got = gpu_decode(torch, w, partition_size=ps)
+        assert (got[1] == 0).all()
+        assert_close(got, oracle_decode(w), "bf16", f"empty sequence, partition {ps}")
+
+
+def test_workspace_too_small_is_rejected():
+    torch = torch_cuda()
+    import paged_kv_cache_288_amd as pkv
+    w = make_workload("splitk", B=1, lens=("fixed", [2000]))
+    dev = to_device(torch, w)
+    out = torch.empty((1, 64, 128), dtype=torch.float32, device="cuda")
+    small = torch.empty(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.paged_decode_attn(out, dev["q"], dev["k_pool"], dev["v_pool"], dev["block_table"],
+                              dev["context_lens"], w.scale, w.max_context_len, partition_size=512,
+                              workspace=small)
+    assert e.value.status == -6
