@@ -47,7 +47,8 @@ def test_decode_every_partition_size(ps):
 @pytest.mark.parametrize("name", ["gqa70b", "tiny"])
 def test_decode_group_sizes(name, heads):
     torch = torch_cuda()
-    w = make_workload(name, seed=7, B=3, lens=("uniform", 1, 700), heads=heads)
+    w = make_workload(name, seed=7, B=3, lens=("uniform", 1, 700), heads=heads,
+                      pool=("factor", 1.25))
     log(f"[decode] {name} heads={heads} lens={w.context_lens.tolist()}")
     assert_close(gpu_decode(torch, w), oracle_decode(w), "bf16", f"{name} heads {heads}")
 
