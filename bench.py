@@ -5,6 +5,9 @@ A step is the whole hot path over one batch: append each sequence's newest K/V r
 (pkv_paged_decode_attn: the decode kernel and, for split contexts, the partition merge).
 Inputs are seeded synthetic tensors already resident in HBM when timing starts.
 
+Steps rotate over --layers independent copies of the KV cache (one per layer, as in a
+real model), so the 256 MB last-level cache cannot carry one step's KV into the next.
+
 Prints one JSON line.  `value` is KV GB/s for the whole step (algorithmic KV bytes read
 per step / step time); decode tokens/s is reported beside it.  `roofline` covers the
 attention call (decode + merge kernels of one pkv_paged_decode_attn call), timed with HIP
@@ -118,6 +121,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gqa70b")
     ap.add_argument("--partition", type=int, default=None)
+    ap.add_argument("--layers", type=int, default=4,
+                    help="copies of the KV cache the steps rotate over (one step = one layer)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--flush", action="store_true",
                     help="write 512 MiB of scratch before every step (outside the call's events)")
@@ -153,7 +158,9 @@ def main():
         a = a.view(np.int16) if a.dtype == np.uint16 else a
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    q, kp, vp = put(w.q), put(w.k_pool), put(w.v_pool)
+    q, kp0, vp0 = put(w.q), put(w.k_pool), put(w.v_pool)
+    kps = [kp0] + [kp0.clone() for _ in range(args.layers - 1)]
+    vps = [vp0] + [None if vp0 is None else vp0.clone() for _ in range(args.layers - 1)]
     bt, cl = put(w.block_table), put(w.context_lens)
     ks, vs = put(w.k_scale), put(w.v_scale)
     nk, nv, slots = put(w.new_k), put(w.new_v), put(w.slot_mapping)
@@ -167,7 +174,7 @@ def main():
     flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.flush else None
     torch.cuda.synchronize()
 
-    def attend():
+    def attend(kp, vp):
         if w.kind == "mla":
             pkv.paged_decode_attn_mla(out, q, kp, bt, cl, w.scale, w.max_context_len, d_v=w.d_v,
                                       partition_size=ps, workspace=ws)
@@ -176,18 +183,19 @@ def main():
                                   kv_dtype=w.kv_dtype, k_scale=ks, v_scale=vs,
                                   partition_size=ps, workspace=ws)
 
-    def step(ev=None):
+    def step(i, ev=None):
+        kp, vp = kps[i % args.layers], vps[i % args.layers]
         if flush_buf is not None:
             flush_buf.fill_(1)
         pkv.kv_append(kp, vp, nk, nv, slots, kv_dtype=w.kv_dtype)
         if ev is not None:
             ev[0].record()
-        attend()
+        attend(kp, vp)
         if ev is not None:
             ev[1].record()
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
 
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -196,7 +204,7 @@ def main():
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
-        step(evs[i])
+        step(args.warmup + i, evs[i])
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
@@ -234,6 +242,7 @@ def main():
             "partition_size": int(pkv.decode_partition_size(w.B, w.Hkv, w.max_context_len, ps))
             if w.kind != "mla" else ps,
             "kv_bytes_per_step": kvb, "flush_between_steps": bool(args.flush),
+            "cache_copies_rotated": args.layers,
         },
         "decode_tokens_per_s": round(w.B / (ms_per_step * 1e-3), 1),
         "hbm_peak_frac_step": round(kvb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -30,6 +30,18 @@ int32_t auto_partition(int32_t B, int32_t heads, int32_t max_ctx) {
   return ps;
 }
 
+// Latent decode: one workgroup covers 64 query heads of a partition, and a partition's
+// partial output (128 heads x 512 fp32) is large next to its latent rows, so split only
+// as far as needed for about two workgroups per CU.
+int32_t mla_auto_partition(int32_t B, int32_t Hq, int32_t max_ctx) {
+  const long long groups = (long long)B * ((Hq + 63) / 64);
+  long long parts = (2 * 256 + groups - 1) / (groups > 0 ? groups : 1);
+  if (parts < 1) parts = 1;
+  long long ps = (max_ctx + parts - 1) / parts;
+  ps = (ps + 63) / 64 * 64;
+  return (int32_t)(ps < 64 ? 64 : ps);
+}
+
 int32_t num_parts(int32_t max_ctx, int32_t ps) {
   const int32_t p = (max_ctx + ps - 1) / ps;
   return p < 1 ? 1 : p;
@@ -165,7 +177,7 @@ pkv_status pkv_paged_decode_attn(float* out, const void* q, const void* k_pool,
 size_t pkv_mla_workspace_bytes(int32_t B, int32_t Hq, int32_t d_v, int32_t max_context_len,
                                int32_t partition_size) {
   if (B < 0 || Hq <= 0 || d_v <= 0 || max_context_len < 0 || partition_size < 0) return 0;
-  const int32_t ps = partition_size > 0 ? partition_size : auto_partition(B, 1, max_context_len);
+  const int32_t ps = partition_size > 0 ? partition_size : mla_auto_partition(B, Hq, max_context_len);
   return ws_bytes(B, Hq, d_v, num_parts(max_context_len, ps));
 }
 
@@ -190,7 +202,7 @@ pkv_status pkv_paged_decode_attn_mla(float* out, const void* q, const void* kv_p
     return PKV_ERR_ALIGN;
   if (B > kGridYZMax) return PKV_ERR_SHAPE;
   const int32_t ctx = max_context_len;
-  const int32_t ps = partition_size > 0 ? partition_size : auto_partition(B, 1, ctx);
+  const int32_t ps = partition_size > 0 ? partition_size : mla_auto_partition(B, Hq, ctx);
   const int32_t P = num_parts(ctx, ps);
   if (P > kGridYZMax) return PKV_ERR_SHAPE;
   float *ws_m = nullptr, *ws_l = nullptr, *ws_o = nullptr;
