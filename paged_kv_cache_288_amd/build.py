@@ -14,6 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpkv.so")
+READ_CEILING = os.path.join(HERE, "read_ceiling")   # standalone bandwidth probe
 ARCH = "gfx950"
 
 SOURCES = ["pkv_api.hip", "kv_append.hip", "gqa_decode.hip", "mla_decode.hip"]
@@ -54,8 +55,13 @@ def build(isa=False, verbose=True):
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    cmd = [HIPCC, *FLAGS, os.path.join(CSRC, "read_ceiling.hip"), "-o", READ_CEILING + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for read_ceiling.hip:\n{r.stderr}")
+    os.replace(READ_CEILING + ".tmp", READ_CEILING)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {READ_CEILING}")
     return LIB
 
 

@@ -1,0 +1,66 @@
+// Achievable HBM read bandwidth on this GPU: a grid-stride kernel reading a 4 GiB buffer
+// with 16-byte loads (plain and nontemporal), for comparison with the decode kernels.
+// Usage: read_ceiling   (prints one line per configuration, GB/s)
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+
+template <int UNROLL, bool NT>
+__global__ void read_kernel(const u32x4* __restrict__ p, size_t n16, uint32_t* out) {
+  size_t i = (size_t)blockIdx.x * blockDim.x * UNROLL + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x * UNROLL;
+  uint32_t acc = 0;
+  for (; i + (size_t)(UNROLL - 1) * blockDim.x < n16; i += stride) {
+    u32x4 v[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u)
+      v[u] = NT ? __builtin_nontemporal_load(p + i + u * blockDim.x) : p[i + u * blockDim.x];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  if (acc == 0x12345678u) out[blockIdx.x] = acc;  // keeps the loads live
+}
+
+template <int U, bool NT>
+static void run(const u32x4* p, size_t n16, uint32_t* out, int blocks) {
+  hipEvent_t a, b;
+  (void)hipEventCreate(&a);
+  (void)hipEventCreate(&b);
+  for (int w = 0; w < 2; ++w)
+    hipLaunchKernelGGL((read_kernel<U, NT>), dim3(blocks), dim3(256), 0, 0, p, n16, out);
+  (void)hipEventRecord(a);
+  const int iters = 10;
+  for (int w = 0; w < iters; ++w)
+    hipLaunchKernelGGL((read_kernel<U, NT>), dim3(blocks), dim3(256), 0, 0, p, n16, out);
+  (void)hipEventRecord(b);
+  (void)hipEventSynchronize(b);
+  float ms = 0.f;
+  (void)hipEventElapsedTime(&ms, a, b);
+  printf("loads=%s unroll=%d workgroups=%d: %.1f GB/s\n", NT ? "nontemporal" : "plain", U, blocks,
+         n16 * 16.0 * iters / (ms * 1e-3) / 1e9);
+  (void)hipEventDestroy(a);
+  (void)hipEventDestroy(b);
+}
+
+int main() {
+  const size_t bytes = 4ull << 30, n16 = bytes / 16;
+  u32x4* p = nullptr;
+  uint32_t* out = nullptr;
+  if (hipMalloc(&p, bytes) != hipSuccess || hipMalloc(&out, 8192 * sizeof(uint32_t)) != hipSuccess) {
+    printf("allocation failed\n");
+    return 1;
+  }
+  (void)hipMemset(p, 1, bytes);
+  (void)hipDeviceSynchronize();
+  for (int blocks : {1024, 2048, 4096, 8192}) {
+    run<4, false>(p, n16, out, blocks);
+    run<8, false>(p, n16, out, blocks);
+    run<4, true>(p, n16, out, blocks);
+  }
+  (void)hipFree(p);
+  (void)hipFree(out);
+  return 0;
+}
