@@ -138,18 +138,37 @@ struct WaveState {
   float l;                            // running sum of probabilities, head c, this group
 };
 
+// K and V of a tile are streamed once and never re-read: nontemporal loads keep them from
+// displacing q, block-table and partial data in the caches.
+__device__ __forceinline__ uint4 load_nt16(const uint8_t* p) {
+  typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return uint4{v[0], v[1], v[2], v[3]};
+}
+__device__ __forceinline__ uint2 load_nt8(const uint8_t* p) {
+  typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+  const u32x2 v = __builtin_nontemporal_load((const u32x2*)p);
+  return uint2{v[0], v[1]};
+}
+
 template <int D, bool FP8>
-__device__ __forceinline__ void load_tile(TileRegs<D, FP8>& R, const uint8_t* kt,
-                                          const uint8_t* vt, int k, int c, int r, int dc) {
+__device__ __forceinline__ void load_k(TileRegs<D, FP8>& R, const uint8_t* kt, int k, int c) {
   using Lo = Layout<D, FP8>;
 #pragma unroll
   for (int pi = 0; pi < 2; ++pi)
 #pragma unroll
     for (int j = 0; j < Lo::KL; ++j)
-      R.k[pi][j] = *(const uint4*)(kt + (8 * pi + k) * Lo::ROW + j * 128 + 16 * c);
+      R.k[pi][j] = load_nt16(kt + (8 * pi + k) * Lo::ROW + j * 128 + 16 * c);
+}
+template <int D, bool FP8>
+__device__ __forceinline__ void load_v(TileRegs<D, FP8>& R, const uint8_t* vt, int r, int dc) {
+  using Lo = Layout<D, FP8>;
 #pragma unroll
-  for (int u = 0; u < Lo::TPG; ++u)
-    R.v[u] = *(const typename VReg<FP8>::T*)(vt + pv_token<D>(u, r) * Lo::ROW + dc * Lo::VB);
+  for (int u = 0; u < Lo::TPG; ++u) {
+    const uint8_t* p = vt + pv_token<D>(u, r) * Lo::ROW + dc * Lo::VB;
+    if constexpr (FP8) R.v[u] = load_nt8(p);
+    else R.v[u] = load_nt16(p);
+  }
 }
 
 template <int D, int G, bool FP8, int H>
@@ -179,13 +198,16 @@ __device__ __forceinline__ void pv_all(WaveState<D, G, FP8>& S, uint32_t pair,
   (pv_head<D, G, FP8, Hs>(S, pair, vp, lane), ...);
 }
 
-// One 16-token tile: scores, online-softmax update, p.V accumulation.
-// nv = number of valid tokens in the tile (16 for all but a sequence's last tile).
+// First half of a 16-token tile: scores and the online-softmax update; returns the
+// probabilities as bf16 token pairs (in `pairs`).  Consumes only R.k, so the caller can
+// refill R.k before the second half.  nv = valid tokens in the tile (16 except a
+// sequence's last tile).
 template <int D, int G, bool FP8>
-__device__ __forceinline__ void process_tile(WaveState<D, G, FP8>& S, TileRegs<D, FP8>& R,
-                                             int nv, float cscale, int lane) {
+__device__ __forceinline__ void qk_softmax(WaveState<D, G, FP8>& S, const TileRegs<D, FP8>& R,
+                                           int nv, float cscale, int lane,
+                                           uint32_t (&pairs)[Layout<D, FP8>::NPS]) {
   using Lo = Layout<D, FP8>;
-  const int k = lane >> 3, c = lane & 7, r = lane / Lo::LPT;
+  const int k = lane >> 3, c = lane & 7;
   const bool partial = nv < kTile;
   constexpr auto heads = std::make_integer_sequence<int, G>{};
 
@@ -237,7 +259,6 @@ __device__ __forceinline__ void process_tile(WaveState<D, G, FP8>& S, TileRegs<D
   const float p0 = fast_exp2(s[0] - m_use), p1 = fast_exp2(s[1] - m_use);
 
   // ---- probability pairs (two tokens of a p.V pair slot) as bf16, and the running sum
-  uint32_t pairs[Lo::NPS];
   if constexpr (D == 128) {
     pairs[0] = pack_bf16(p0, dpp<kDppRowRor8>(p0));
     pairs[1] = pack_bf16(p1, dpp<kDppRowRor8>(p1));
@@ -248,8 +269,17 @@ __device__ __forceinline__ void process_tile(WaveState<D, G, FP8>& S, TileRegs<D
     S.l = dot2(pairs[0], kOnesBf16x2, S.l);
   }
 
-  // ---- p.V
-  if (partial) {
+}
+
+// Second half of a tile: p.V accumulation.  Consumes only R.v.
+template <int D, int G, bool FP8>
+__device__ __forceinline__ void pv_accumulate(WaveState<D, G, FP8>& S, TileRegs<D, FP8>& R,
+                                              int nv, int lane,
+                                              const uint32_t (&pairs)[Layout<D, FP8>::NPS]) {
+  using Lo = Layout<D, FP8>;
+  const int r = lane / Lo::LPT;
+  constexpr auto heads = std::make_integer_sequence<int, G>{};
+  if (nv < kTile) {
 #pragma unroll
     for (int u = 0; u < Lo::TPG; ++u)
       if (pv_token<D>(u, r) >= nv) R.v[u] = typename VReg<FP8>::T{};
@@ -336,41 +366,21 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void gqa_decode_kernel(DecodeArg
   const int g = blockIdx.x, part = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int k = lane >> 3, c = lane & 7, r = lane / Lo::LPT, dc = lane % Lo::LPT;
-
-  int L = a.context_lens[b];
-  L = L < 0 ? 0 : (L > a.max_blocks * a.block_size ? a.max_blocks * a.block_size : L);
   const int t0 = part * a.partition;
-  if (t0 >= L) {
-    if (a.num_partitions == 1 && part == 0) {  // empty sequence: output 0
-      for (int idx = threadIdx.x; idx < G * D; idx += kWaves * kWave)
-        a.out[((size_t)b * a.Hq + (size_t)g * G) * D + idx] = 0.f;
-    }
-    return;
-  }
-  const int t1 = min(L, t0 + a.partition);
-  const int tile_begin = t0 / kTile, tile_end = (t1 + kTile - 1) / kTile;
-  const int nt = tile_end - tile_begin > w ? (tile_end - tile_begin - w + kWaves - 1) / kWaves : 0;
   const int tiles_per_block = a.block_size / kTile;
-
-  // Byte offset (within a head's pool slice) and valid-token count of this wave's tiles,
-  // one tile per lane (at most 64 tiles per wave).  A block id outside the pool is never
-  // dereferenced: its tile reads block 0 and counts no valid token.
+  const int tile_begin = t0 / kTile;
   const size_t head_bytes = (size_t)a.block_size * Lo::ROW;
   const size_t block_bytes = head_bytes * a.Hkv;
-  uint32_t off_lo = 0, off_hi = 0;
-  int nv_lane = 0;
-  if (lane < nt) {
-    const int tile = tile_begin + w + kWaves * lane;
-    const int phys = a.block_table[(size_t)b * a.max_blocks + tile / tiles_per_block];
-    const bool ok = (unsigned)phys < (unsigned)a.num_blocks;
-    const uint64_t off = (uint64_t)(ok ? phys : 0) * block_bytes +
-                         (uint64_t)(tile % tiles_per_block) * (kTile * Lo::ROW);
-    off_lo = (uint32_t)off;
-    off_hi = (uint32_t)(off >> 32);
-    nv_lane = ok ? min(kTile, t1 - tile * kTile) : 0;
-  }
-  const uint8_t* kbase = a.k_pool + (size_t)g * head_bytes;
-  const uint8_t* vbase = a.v_pool + (size_t)g * head_bytes;
+
+  // Issued before the sequence length is known, so the three loads overlap: this wave's
+  // block ids (one tile per lane, at most 64 tiles per wave; the table row is readable up
+  // to max_blocks entries whatever the length), the length, and q.
+  const int my_tile = tile_begin + w + kWaves * lane;
+  const int nt_full = (a.partition / kTile - w + kWaves - 1) / kWaves;
+  int phys = -1;
+  if (lane < nt_full && my_tile / tiles_per_block < a.max_blocks)
+    phys = a.block_table[(size_t)b * a.max_blocks + my_tile / tiles_per_block];
+  int L = a.context_lens[b];
 
   WaveState<D, G, FP8> S;
   // q pairs for this lane's dims (same dims as its K pieces)
@@ -398,6 +408,34 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void gqa_decode_kernel(DecodeArg
   }
   S.m = kNegInf;
   S.l = 0.f;
+
+  L = L < 0 ? 0 : (L > a.max_blocks * a.block_size ? a.max_blocks * a.block_size : L);
+  if (t0 >= L) {
+    if (a.num_partitions == 1 && part == 0) {  // empty sequence: output 0
+      for (int idx = threadIdx.x; idx < G * D; idx += kWaves * kWave)
+        a.out[((size_t)b * a.Hq + (size_t)g * G) * D + idx] = 0.f;
+    }
+    return;
+  }
+  const int t1 = min(L, t0 + a.partition);
+  const int tile_end = (t1 + kTile - 1) / kTile;
+  const int nt = tile_end - tile_begin > w ? (tile_end - tile_begin - w + kWaves - 1) / kWaves : 0;
+
+  // Byte offset (within a head's pool slice) and valid-token count of this wave's tiles,
+  // one tile per lane.  A block id outside the pool is never dereferenced: its tile reads
+  // block 0 and counts no valid token.
+  uint32_t off_lo = 0, off_hi = 0;
+  int nv_lane = 0;
+  if (lane < nt) {
+    const bool ok = (unsigned)phys < (unsigned)a.num_blocks;
+    const uint64_t off = (uint64_t)(ok ? phys : 0) * block_bytes +
+                         (uint64_t)(my_tile % tiles_per_block) * (kTile * Lo::ROW);
+    off_lo = (uint32_t)off;
+    off_hi = (uint32_t)(off >> 32);
+    nv_lane = ok ? min(kTile, t1 - my_tile * kTile) : 0;
+  }
+  const uint8_t* kbase = a.k_pool + (size_t)g * head_bytes;
+  const uint8_t* vbase = a.v_pool + (size_t)g * head_bytes;
   const float cscale = a.scale * kLog2e * (FP8 ? a.k_scale[g] : 1.f);
 
   auto tile_addr = [&](int n, const uint8_t*& kt, const uint8_t*& vt) -> int {
@@ -408,25 +446,48 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void gqa_decode_kernel(DecodeArg
     return __builtin_amdgcn_readlane(nv_lane, n);
   };
 
+  // Two tile buffers, refilled half by half: a tile's K is replaced by the tile two ahead
+  // as soon as its scores are done, its V once p.V is done, so one and a half to two tiles
+  // are always in flight.
   TileRegs<D, FP8> RA, RB;
-  const uint8_t *kt, *vt;
+  const uint8_t *ktA, *vtA, *ktB, *vtB;
   int nvA = 0, nvB = 0;
   if (nt > 0) {
-    nvA = tile_addr(0, kt, vt);
-    load_tile<D, FP8>(RA, kt, vt, k, c, r, dc);
+    nvA = tile_addr(0, ktA, vtA);
+    load_k<D, FP8>(RA, ktA, k, c);
+    load_v<D, FP8>(RA, vtA, r, dc);
+  }
+  if (nt > 1) {
+    nvB = tile_addr(1, ktB, vtB);
+    load_k<D, FP8>(RB, ktB, k, c);
+    load_v<D, FP8>(RB, vtB, r, dc);
   }
   for (int n = 0; n < nt; n += 2) {
-    if (n + 1 < nt) {
-      nvB = tile_addr(n + 1, kt, vt);
-      load_tile<D, FP8>(RB, kt, vt, k, c, r, dc);
+    {
+      uint32_t pairs[Lo::NPS];
+      qk_softmax<D, G, FP8>(S, RA, nvA, cscale, lane, pairs);
+      int nv_next = 0;
+      if (n + 2 < nt) {
+        nv_next = tile_addr(n + 2, ktA, vtA);
+        load_k<D, FP8>(RA, ktA, k, c);
+      }
+      pv_accumulate<D, G, FP8>(S, RA, nvA, lane, pairs);
+      if (n + 2 < nt) load_v<D, FP8>(RA, vtA, r, dc);
+      nvA = nv_next;
     }
-    process_tile<D, G, FP8>(S, RA, nvA, cscale, lane);
     if (n + 1 >= nt) break;
-    if (n + 2 < nt) {
-      nvA = tile_addr(n + 2, kt, vt);
-      load_tile<D, FP8>(RA, kt, vt, k, c, r, dc);
+    {
+      uint32_t pairs[Lo::NPS];
+      qk_softmax<D, G, FP8>(S, RB, nvB, cscale, lane, pairs);
+      int nv_next = 0;
+      if (n + 3 < nt) {
+        nv_next = tile_addr(n + 3, ktB, vtB);
+        load_k<D, FP8>(RB, ktB, k, c);
+      }
+      pv_accumulate<D, G, FP8>(S, RB, nvB, lane, pairs);
+      if (n + 3 < nt) load_v<D, FP8>(RB, vtB, r, dc);
+      nvB = nv_next;
     }
-    process_tile<D, G, FP8>(S, RB, nvB, cscale, lane);
   }
 
   // ---- merge the wave's row groups: every lane ends with the wave's state for its dims
@@ -491,7 +552,20 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void gqa_decode_kernel(DecodeArg
   }
 }
 
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) x = fmaxf(x, __shfl_xor(x, s));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) x += __shfl_xor(x, s);
+  return x;
+}
+
 // out[b][h] = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p over the sequence's partitions.
+// One wave per (sequence, head): the partitions' statistics are loaded one per lane, their
+// factors broadcast by readlane while the lanes stream the partial outputs.
 template <int D>
 __global__ __launch_bounds__(kWave) void partition_merge_kernel(
     const float* __restrict__ ws_m, const float* __restrict__ ws_l,
@@ -510,15 +584,26 @@ __global__ __launch_bounds__(kWave) void partition_merge_kernel(
   }
   const size_t base = (size_t)bh * P;
   float M = kNegInf;
-  for (int p = 0; p < nP; ++p) M = fmaxf(M, ws_m[base + p]);
+  for (int p0 = 0; p0 < nP; p0 += kWave)
+    if (p0 + lane < nP) M = fmaxf(M, ws_m[base + p0 + lane]);
+  M = wave_max(M);
   float acc[PER] = {};
   float den = 0.f;
-  for (int p = 0; p < nP; ++p) {
-    const float mp = ws_m[base + p];
-    const float f = (mp == kNegInf) ? 0.f : fast_exp2(mp - M);
-    den += f * ws_l[base + p];
+  for (int p0 = 0; p0 < nP; p0 += kWave) {
+    float f = 0.f, lp = 0.f;
+    if (p0 + lane < nP) {
+      const float mp = ws_m[base + p0 + lane];
+      lp = ws_l[base + p0 + lane];
+      f = (mp == kNegInf) ? 0.f : fast_exp2(mp - M);
+    }
+    den += wave_sum(f * lp);
+    const int cnt = min(kWave, nP - p0);
+    const float* op = ws_o + (base + p0) * D + lane;
+    for (int j = 0; j < cnt; ++j) {
+      const float fj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j));
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] += f * ws_o[(base + p) * D + lane + kWave * i];
+      for (int i = 0; i < PER; ++i) acc[i] += fj * op[(size_t)j * D + kWave * i];
+    }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
 #pragma unroll

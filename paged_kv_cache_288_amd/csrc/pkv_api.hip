@@ -10,7 +10,7 @@ namespace {
 
 constexpr int kMaxPartitionTokens = 4096;  // 64 tiles of 16 tokens per wave, 4 waves
 constexpr int kGridYZMax = 65535;
-constexpr long long kTargetWorkgroups = 2048;  // ~8 workgroups per CU on 256 CUs
+constexpr long long kTargetWorkgroups = 1024;  // ~4 workgroups per CU on 256 CUs
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
@@ -20,8 +20,10 @@ int elem_bytes(int32_t dtype) {
   return dtype == PKV_BF16 ? 2 : (dtype == PKV_FP8_E4M3 ? 1 : 0);
 }
 
+// Longest partition (up to 1024 tokens) that still gives every CU several workgroups:
+// each workgroup pays a fixed start (table, q, first tile latency) and end (merge) cost.
 int32_t auto_partition(int32_t B, int32_t heads, int32_t max_ctx) {
-  int32_t ps = 512;
+  int32_t ps = 1024;
   while (ps > 64) {
     const long long parts = (max_ctx + ps - 1) / ps;
     if ((long long)B * heads * (parts > 0 ? parts : 1) >= kTargetWorkgroups) break;

@@ -105,11 +105,11 @@ def test_partition_and_workspace_sizing(lib):
     assert lib.pkv_decode_workspace_bytes(4, 64, 8, 128, 32768, 512) == 2 * r256(rows * 4) + r256(rows * 128 * 4)
     # no split needed -> no workspace
     assert lib.pkv_decode_workspace_bytes(4, 64, 8, 128, 512, 512) == 0
-    # automatic choice fills the GPU: a power of two in [64, 512]
+    # automatic choice fills the GPU: a power of two in [64, 1024]
     for B, H, ctx in [(64, 8, 8192), (2, 1, 256), (1, 8, 32768), (128, 8, 6144)]:
         ps = lib.pkv_decode_partition_size(B, H, ctx, 0)
-        assert ps in (64, 128, 256, 512)
-    assert lib.pkv_decode_partition_size(64, 8, 8192, 0) == 512
+        assert ps in (64, 128, 256, 512, 1024)
+    assert lib.pkv_decode_partition_size(64, 8, 8192, 0) == 1024
     assert lib.pkv_decode_partition_size(2, 1, 256, 0) == 64
     assert lib.pkv_decode_partition_size(1, 8, 100, 20) < 0
 
