@@ -91,18 +91,23 @@ pkv_status pkv_kv_append(void* k_pool, void* v_pool, const void* k_new, const vo
                          void* stream);
 
 /*
- * pkv_decode_partition_size — the context partition (tokens) that pkv_paged_decode_attn
- * will use for these arguments: `partition_size` itself when > 0, otherwise the
- * library's choice for filling the GPU (a power of two, >= 64).  A result >=
- * max_context_len means the context is not split.  Negative = error code.
+ * pkv_decode_partition_size — how pkv_paged_decode_attn divides the work for these
+ * arguments.  With partition_size > 0 each sequence's context is cut into partitions of
+ * that many tokens (a result >= max_context_len means no split).  With partition_size = 0
+ * the result is 0: the balanced mode, where the cached tiles of all (KV head, sequence)
+ * pairs are laid end to end and cut into equal ranges, one per wave of the current device
+ * (B up to 4096; larger batches fall back to a library-chosen partition, which is then
+ * returned).  Negative = error code.
  */
 int32_t pkv_decode_partition_size(int32_t B, int32_t Hkv, int32_t max_context_len,
                                   int32_t partition_size);
 
 /*
  * pkv_decode_workspace_bytes — bytes of workspace pkv_paged_decode_attn needs for these
- * arguments (0 when the context is not split).  The workspace holds, per (sequence,
- * query head, partition), the partition's running max, sum and unnormalised output.
+ * arguments on the current device (0 when a partitioned context is not split).  The
+ * workspace holds the partial online-softmax states (running max, sum and unnormalised
+ * output per query head) of partitions, or of the balanced mode's pieces, plus (balanced
+ * mode) the per-sequence tile prefix the merge step reads.
  */
 size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d_v,
                                   int32_t max_context_len, int32_t partition_size);
@@ -129,13 +134,16 @@ size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d_
  *   block_table  [B][max_blocks_per_seq] int32 (entries past a sequence's end unused)
  *   context_lens [B] int32
  *   max_context_len   host-side upper bound of context_lens (sizes the grid)
- *   partition_size    tokens per partition, a multiple of 16, or 0 for the library's
- *                     choice (see pkv_decode_partition_size)
- *   workspace, workspace_bytes  >= pkv_decode_workspace_bytes(...) when the context is
- *                     split; may be NULL/0 otherwise.
+ *   partition_size    tokens per partition (a multiple of 16, at most 4096), or 0 for the
+ *                     balanced mode (see pkv_decode_partition_size)
+ *   workspace, workspace_bytes  >= pkv_decode_workspace_bytes(...) with the same
+ *                     arguments on the same device; may be NULL/0 when that is 0.
  * Supported: d = 128 with bf16 or FP8 pools, d = 64 with bf16 pools; block_size a
  * multiple of 16 (16, 32, 64, ...); Hq / Hkv in {1, 2, 4, 8}.  Other shapes return
  * PKV_ERR_UNSUPPORTED.  q and out must not alias the pools.
+ * Precision: scores accumulate exact bf16 (or widened FP8) products in fp32; the
+ * softmax weights are rounded to fp16 and V widened to fp16 for p.V, accumulated in fp32.
+ * bf16 V values must therefore lie within fp16's range (|v| < 65504); FP8 values always do.
  */
 pkv_status pkv_paged_decode_attn(float* out, const void* q, const void* k_pool,
                                  const void* v_pool, const float* k_scale, const float* v_scale,
@@ -168,6 +176,8 @@ size_t pkv_mla_workspace_bytes(int32_t B, int32_t Hq, int32_t d_v, int32_t max_c
  *   block_table, context_lens, max_context_len, partition_size, workspace: as above
  *   (partition_size a multiple of block_size, or 0 for the library's choice).
  * Supported: d_qk = 576, d_v = 512, block_size = 64, Hq a multiple of 16 (<= 128).
+ * Precision: scores on the bf16 MFMA (fp32 accumulate); weights and the value dims in fp16
+ * on the fp16 MFMA for p.V, so latent values must satisfy |v| < 65504.
  */
 pkv_status pkv_paged_decode_attn_mla(float* out, const void* q, const void* kv_pool,
                                      const int32_t* block_table, const int32_t* context_lens,

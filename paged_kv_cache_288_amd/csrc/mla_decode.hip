@@ -6,18 +6,21 @@
 // attend to it, using the whole row as key and its first 512 dims as value:
 //     out[b][h] = softmax_t(scale * q[b][h] . C_t) C_t[0:512].
 // With 128 heads sharing each latent row this is a dense contraction (about 240 flop
-// per byte read), so both products run on MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulate).
+// per byte read), so both products run on MFMA (v_mfma_f32_16x16x32_bf16 for the scores,
+// v_mfma_f32_16x16x32_f16 for P V; fp32 accumulate).
 //
 // Work decomposition: one workgroup of 4 waves per (sequence, context partition, group of
 // 64 query heads); wave w owns 16 heads.  The partition is walked in stages of 32 tokens
 // (half a 64-token block).  Each stage is staged into LDS twice by all 256 threads:
 //  * token-major K[32][576] (rows padded to 1168 bytes): A operand of S^T = K Q^T, where a
 //    lane needs 8 consecutive dims of one token;
-//  * dim-major V^T[512][32] (rows padded to 72 bytes), built with an in-register 8x8
+//  * dim-major V^T[512][32] in fp16 (rows padded to 72 bytes), built with an in-register
 //    transpose: B operand of O = P V, where a lane needs 8 tokens of one dim.
 // Scores are produced transposed (tokens x heads), which leaves each lane holding one head
 // and 8 tokens: after the online-softmax update these 8 probabilities, rounded to bf16, are
-// exactly that lane's A operand for P V, so no data moves between the two products.
+// exactly that lane's A operand for P V, so no data moves between the two products.  P V
+// runs on the fp16 MFMA (probabilities and V in fp16: 10-bit mantissas, so rounding the
+// weights costs 2^-11 relative instead of bf16's 2^-9).
 // The token order inside a P V contraction step is (4g..4g+3, 16+4g..16+4g+3) for lane group
 // g; the V^T reads use the same order.  The running max moves lazily (only when a score
 // exceeds it by more than 2^8).  Partitions of a split context write (m, l, o) partials
@@ -30,6 +33,7 @@ namespace pkv {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 constexpr int kDqk = 576;
@@ -48,6 +52,9 @@ constexpr float kSlack = 8.0f;
 
 __device__ __forceinline__ f32x4_t mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_h(const f16x8_t& a, const f16x8_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ uint32_t dword(const uint4& v, int i) {
@@ -153,13 +160,13 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void mla_decode_kernel(MlaArgs a
         for (int tt = 0; tt < 4; ++tt)
           *(uint4*)(ldsK + (4 * tq + tt) * kKStride + dc * 16) = X[tt];
 #pragma unroll
-        for (int dd2 = 0; dd2 < 4; ++dd2) {
+        for (int dd2 = 0; dd2 < 4; ++dd2) {  // V^T is kept in fp16 (exact for |v| < 65504)
           const uint32_t x0 = dword(X[0], dd2), x1 = dword(X[1], dd2);
           const uint32_t x2 = dword(X[2], dd2), x3 = dword(X[3], dd2);
           uint8_t* r0 = ldsVt + (8 * dc + 2 * dd2) * kVtStride + tq * 8;
-          *(uint2*)(r0) = uint2{byte_perm(x1, x0, 0x05040100u), byte_perm(x3, x2, 0x05040100u)};
+          *(uint2*)(r0) = uint2{pack_f16(bf16_lo(x0), bf16_lo(x1)), pack_f16(bf16_lo(x2), bf16_lo(x3))};
           *(uint2*)(r0 + kVtStride) =
-              uint2{byte_perm(x1, x0, 0x07060302u), byte_perm(x3, x2, 0x07060302u)};
+              uint2{pack_f16(bf16_hi(x0), bf16_hi(x1)), pack_f16(bf16_hi(x2), bf16_hi(x3))};
         }
       }
       // RoPE dims 512..575: thread -> (token tid/8, chunk tid%8)
@@ -212,13 +219,14 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void mla_decode_kernel(MlaArgs a
       }
     }
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+    // probabilities in fp16 (p <= 2^8 after the lazy max; 2^-11 relative rounding)
     uint32_t pp[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      pp[j] = pack_bf16(fast_exp2(sv[2 * j] - m_use), fast_exp2(sv[2 * j + 1] - m_use));
+      pp[j] = pack_f16(fast_exp2(sv[2 * j] - m_use), fast_exp2(sv[2 * j + 1] - m_use));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) l_part = dot2(pp[j], kOnesBf16x2, l_part);
-    const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, uint4{pp[0], pp[1], pp[2], pp[3]});
+    for (int j = 0; j < 4; ++j) l_part = dot2h(pp[j], kOnesF16x2, l_part);
+    const f16x8_t pf = __builtin_bit_cast(f16x8_t, uint4{pp[0], pp[1], pp[2], pp[3]});
 
     // ---- O += P V over the stage's 32 tokens, 32 tiles of 16 output dims
 #pragma unroll
@@ -226,8 +234,8 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void mla_decode_kernel(MlaArgs a
       const uint8_t* vrow = ldsVt + (16 * n + c16) * kVtStride;
       const uint2 v0 = *(const uint2*)(vrow + 8 * g);        // tokens 4g..4g+3
       const uint2 v1 = *(const uint2*)(vrow + 32 + 8 * g);   // tokens 16+4g..16+4g+3
-      const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, uint4{v0.x, v0.y, v1.x, v1.y});
-      o[n] = mfma(pf, vf, o[n]);
+      const f16x8_t vf = __builtin_bit_cast(f16x8_t, uint4{v0.x, v0.y, v1.x, v1.y});
+      o[n] = mfma_h(pf, vf, o[n]);
     }
   }
   if (!active) return;

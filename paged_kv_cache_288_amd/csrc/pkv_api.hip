@@ -9,6 +9,8 @@
 namespace {
 
 constexpr int kMaxPartitionTokens = 4096;  // 64 tiles of 16 tokens per wave, 4 waves
+constexpr int kMaxStreamSeqs = 4096;       // balanced mode: sequences per call
+constexpr long long kMaxChunkTiles = 128;  // balanced mode: tiles per wave
 constexpr int kGridYZMax = 65535;
 constexpr long long kTargetWorkgroups = 1024;  // ~4 workgroups per CU on 256 CUs
 
@@ -65,6 +67,43 @@ void ws_split(void* ws, int32_t B, int32_t Hq, int32_t P, float** m, float** l, 
   *o = (float*)(base + 2 * round256(rows * sizeof(float)));
 }
 
+// Compute units of the current device (cached per device; 256 on MI355X).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Balanced mode: one chunk per wave, two 4-wave workgroups per CU, and enough chunks that
+// none holds more than kMaxChunkTiles tiles even if every context were max_context_len.
+int32_t stream_chunks(int32_t B, int32_t Hkv, int32_t max_ctx) {
+  const long long tmax = (long long)Hkv * B * ((max_ctx + 15) / 16);
+  long long c = 8LL * device_cus();
+  const long long need = (tmax + kMaxChunkTiles - 1) / kMaxChunkTiles;
+  if (need > c) c = need;
+  c = (c + 31) / 32 * 32;
+  return c > (1LL << 30) ? -1 : (int32_t)c;
+}
+
+// Balanced-mode workspace: m [S][G], l [S][G], o [S][G][d], prefix [B + 1] (int32),
+// S = chunks + Hkv * B piece slots; sections 256-byte aligned.
+size_t stream_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t chunks) {
+  const size_t rows = ((size_t)chunks + (size_t)Hkv * B) * (size_t)(Hq / Hkv);
+  return 2 * round256(rows * sizeof(float)) + round256(rows * d * sizeof(float)) +
+         round256(((size_t)B + 1) * sizeof(int32_t));
+}
+
+bool stream_mode(int32_t B, int32_t partition_size) {
+  return partition_size == 0 && B <= kMaxStreamSeqs;
+}
+
 pkv_status hip_status(hipError_t e) {
   if (e == hipSuccess) return PKV_OK;
   if (e == hipErrorNotSupported) return PKV_ERR_UNSUPPORTED;
@@ -115,13 +154,19 @@ int32_t pkv_decode_partition_size(int32_t B, int32_t Hkv, int32_t max_context_le
   if (B < 0 || Hkv <= 0 || max_context_len < 0) return PKV_ERR_SHAPE;
   if (partition_size < 0 || partition_size % 16 || partition_size > kMaxPartitionTokens)
     return PKV_ERR_SHAPE;
+  // balanced mode packs (segment << 5) into 32 bits: Hkv * B must stay below 2^26
+  if (stream_mode(B, partition_size) && (long long)Hkv * B < (1LL << 26)) return 0;
   return partition_size > 0 ? partition_size : auto_partition(B, Hkv, max_context_len);
 }
 
 size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d_v,
                                   int32_t max_context_len, int32_t partition_size) {
   const int32_t ps = pkv_decode_partition_size(B, Hkv, max_context_len, partition_size);
-  if (ps <= 0 || Hq <= 0 || d_v <= 0) return 0;
+  if (ps < 0 || Hq <= 0 || d_v <= 0 || Hq % Hkv) return 0;
+  if (ps == 0) {
+    const int32_t chunks = stream_chunks(B, Hkv, max_context_len);
+    return chunks < 0 ? 0 : stream_ws_bytes(B, Hq, Hkv, d_v, chunks);
+  }
   return ws_bytes(B, Hq, d_v, num_parts(max_context_len, ps));
 }
 
@@ -155,7 +200,27 @@ pkv_status pkv_paged_decode_attn(float* out, const void* q, const void* k_pool,
   // each sequence's own length is clamped to its table inside the kernels.
   const int32_t ctx = max_context_len;
   const int32_t ps = pkv_decode_partition_size(B, Hkv, ctx, partition_size);
-  if (ps <= 0) return PKV_ERR_SHAPE;
+  if (ps < 0) return PKV_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  if (ps == 0) {  // balanced mode
+    const int32_t chunks = stream_chunks(B, Hkv, ctx);
+    if (chunks < 0) return PKV_ERR_SHAPE;
+    const size_t need = stream_ws_bytes(B, Hq, Hkv, d, chunks);
+    if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+    const size_t rows = ((size_t)chunks + (size_t)Hkv * B) * (size_t)(Hq / Hkv);
+    char* base = (char*)workspace;
+    float* ws_m = (float*)base;
+    float* ws_l = (float*)(base + round256(rows * sizeof(float)));
+    float* ws_o = (float*)(base + 2 * round256(rows * sizeof(float)));
+    int32_t* ws_p = (int32_t*)(base + 2 * round256(rows * sizeof(float)) +
+                               round256(rows * d * sizeof(float)));
+    pkv::DecodeArgs a{out, (const uint16_t*)q, (const uint8_t*)k_pool, (const uint8_t*)v_pool,
+                      k_scale, v_scale, block_table, context_lens, ws_m, ws_l, ws_o,
+                      B, Hq, Hkv, d, block_size, num_blocks, max_blocks_per_seq, ctx,
+                      0, 0, scale, fp8 ? 1 : 0, chunks, ws_p};
+    return hip_status(pkv::launch_gqa_stream(a, s));
+  }
   const int32_t P = num_parts(ctx, ps);
   if (P > kGridYZMax) return PKV_ERR_SHAPE;
   float *ws_m = nullptr, *ws_l = nullptr, *ws_o = nullptr;
@@ -167,8 +232,7 @@ pkv_status pkv_paged_decode_attn(float* out, const void* q, const void* k_pool,
   pkv::DecodeArgs a{out, (const uint16_t*)q, (const uint8_t*)k_pool, (const uint8_t*)v_pool,
                     k_scale, v_scale, block_table, context_lens, ws_m, ws_l, ws_o,
                     B, Hq, Hkv, d, block_size, num_blocks, max_blocks_per_seq, ctx,
-                    ps, P, scale, fp8 ? 1 : 0};
-  hipStream_t s = (hipStream_t)stream;
+                    ps, P, scale, fp8 ? 1 : 0, 0, nullptr};
   pkv_status st = hip_status(pkv::launch_gqa_decode(a, s));
   if (st != PKV_OK || P == 1) return st;
   return hip_status(pkv::launch_partition_merge(ws_m, ws_l, ws_o, context_lens, out, B, Hq, d,

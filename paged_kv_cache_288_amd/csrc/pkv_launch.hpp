@@ -35,8 +35,14 @@ struct DecodeArgs {
   int32_t partition, num_partitions;  // num_partitions == 1: no split, out written directly
   float scale;
   int32_t fp8;
+  // balanced mode: number of equal chunks (one per wave, a multiple of 32) and the
+  // per-sequence tile prefix [B + 1] the decode kernel leaves for the merge kernel
+  int32_t chunks;
+  int32_t* ws_prefix;
 };
 hipError_t launch_gqa_decode(const DecodeArgs& a, hipStream_t s);
+// Balanced mode: decode kernel + merge kernel (always both).
+hipError_t launch_gqa_stream(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_partition_merge(const float* ws_m, const float* ws_l, const float* ws_o,
                                   const int32_t* context_lens, float* out, int32_t B,
                                   int32_t Hq, int32_t d, int32_t partition,

@@ -24,6 +24,49 @@ __global__ void read_kernel(const u32x4* __restrict__ p, size_t n16, uint32_t* o
   if (acc == 0x12345678u) out[blockIdx.x] = acc;  // keeps the loads live
 }
 
+// Chunked variant: each wave reads whole CHUNK-byte pieces (1 KiB per load instruction) at
+// scattered chunk indices (a fixed odd-multiplier permutation), as a paged KV cache does.
+template <int CHUNK, bool NT>
+__global__ void chunk_kernel(const u32x4* __restrict__ p, size_t nchunks, uint32_t* out) {
+  constexpr int PER = CHUNK / 1024;   // load instructions per chunk per wave
+  const int lane = threadIdx.x & 63;
+  const size_t wave = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const size_t nwaves = ((size_t)gridDim.x * blockDim.x) >> 6;
+  uint32_t acc = 0;
+  for (size_t i = wave; i < nchunks; i += nwaves) {
+    const size_t c = (i * 2654435761ull) % nchunks;   // odd multiplier: a permutation when nchunks is a power of two
+    const u32x4* q = p + c * (CHUNK / 16) + lane;
+    u32x4 v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) v[u] = NT ? __builtin_nontemporal_load(q + u * 64) : q[u * 64];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  if (acc == 0x12345678u) out[blockIdx.x] = acc;
+}
+
+template <int CHUNK, bool NT>
+static void run_chunks(const u32x4* p, size_t bytes, uint32_t* out, int blocks) {
+  const size_t nchunks = bytes / CHUNK;
+  hipEvent_t a, b;
+  (void)hipEventCreate(&a);
+  (void)hipEventCreate(&b);
+  for (int w = 0; w < 2; ++w)
+    hipLaunchKernelGGL((chunk_kernel<CHUNK, NT>), dim3(blocks), dim3(256), 0, 0, p, nchunks, out);
+  (void)hipEventRecord(a);
+  const int iters = 10;
+  for (int w = 0; w < iters; ++w)
+    hipLaunchKernelGGL((chunk_kernel<CHUNK, NT>), dim3(blocks), dim3(256), 0, 0, p, nchunks, out);
+  (void)hipEventRecord(b);
+  (void)hipEventSynchronize(b);
+  float ms = 0.f;
+  (void)hipEventElapsedTime(&ms, a, b);
+  printf("scattered %d KiB chunks, loads=%s workgroups=%d: %.1f GB/s\n", CHUNK / 1024,
+         NT ? "nontemporal" : "plain", blocks, (double)nchunks * CHUNK * iters / (ms * 1e-3) / 1e9);
+  (void)hipEventDestroy(a);
+  (void)hipEventDestroy(b);
+}
+
 template <int U, bool NT>
 static void run(const u32x4* p, size_t n16, uint32_t* out, int blocks) {
   hipEvent_t a, b;
@@ -59,6 +102,12 @@ int main() {
     run<4, false>(p, n16, out, blocks);
     run<8, false>(p, n16, out, blocks);
     run<4, true>(p, n16, out, blocks);
+  }
+  for (int blocks : {2048, 8192}) {
+    run_chunks<4096, false>(p, bytes, out, blocks);
+    run_chunks<4096, true>(p, bytes, out, blocks);
+    run_chunks<8192, true>(p, bytes, out, blocks);
+    run_chunks<16384, true>(p, bytes, out, blocks);
   }
   (void)hipFree(p);
   (void)hipFree(out);

@@ -70,6 +70,7 @@ def decode(lib, **kw):
     (dict(q=MIS), -5), (dict(k=MIS), -5),
     (dict(ctx=8192, ps=512, mb=512), -6),                       # split needs a workspace
     (dict(ctx=8192, ps=512, mb=512, ws=FAKE, wsb=100), -6),     # too small
+    (dict(ctx=8192, ps=0, mb=512), -6),                         # balanced mode needs one too
     (dict(ps=24), -2), (dict(ps=8192), -2),
 ])
 def test_decode_rejects_bad_arguments_before_launch(lib, kw, code):
@@ -105,13 +106,65 @@ def test_partition_and_workspace_sizing(lib):
     assert lib.pkv_decode_workspace_bytes(4, 64, 8, 128, 32768, 512) == 2 * r256(rows * 4) + r256(rows * 128 * 4)
     # no split needed -> no workspace
     assert lib.pkv_decode_workspace_bytes(4, 64, 8, 128, 512, 512) == 0
-    # automatic choice fills the GPU: a power of two in [64, 1024]
+    # partition_size 0 selects the balanced mode (reported as 0) up to 4096 sequences,
+    # beyond which the library picks a partition (a power of two in [64, 1024])
     for B, H, ctx in [(64, 8, 8192), (2, 1, 256), (1, 8, 32768), (128, 8, 6144)]:
-        ps = lib.pkv_decode_partition_size(B, H, ctx, 0)
-        assert ps in (64, 128, 256, 512, 1024)
-    assert lib.pkv_decode_partition_size(64, 8, 8192, 0) == 1024
-    assert lib.pkv_decode_partition_size(2, 1, 256, 0) == 64
+        assert lib.pkv_decode_partition_size(B, H, ctx, 0) == 0
+    assert lib.pkv_decode_partition_size(5000, 8, 256, 0) in (64, 128, 256, 512, 1024)
     assert lib.pkv_decode_partition_size(1, 8, 100, 20) < 0
+
+
+def _stream_chunks(B, Hkv, ctx, cus):
+    tmax = Hkv * B * ((ctx + 15) // 16)
+    c = max(8 * cus, -(-tmax // 128))
+    return -(-c // 32) * 32
+
+
+def test_balanced_mode_workspace_size(lib):
+    r256 = lambda x: (x + 255) // 256 * 256
+    # this container has no GPU: the library assumes 256 CUs when the device query fails
+    for B, Hq, Hkv, d, ctx in [(64, 64, 8, 128, 8192), (2, 4, 1, 64, 256), (4, 64, 8, 128, 32768)]:
+        C = _stream_chunks(B, Hkv, ctx, 256)
+        rows = (C + Hkv * B) * (Hq // Hkv)
+        want = 2 * r256(rows * 4) + r256(rows * d * 4) + r256((B + 1) * 4)
+        assert lib.pkv_decode_workspace_bytes(B, Hq, Hkv, d, ctx, 0) == want
+
+
+def chunk_of(t, T, C):
+    return ((t + 1) * C - 1) // T
+
+
+@pytest.mark.parametrize("lens,Hkv,C", [([7, 0, 300, 1, 16, 17], 2, 32), ([4096] * 3, 8, 64),
+                                        ([1, 1, 1], 1, 32), ([5000, 33], 4, 2048)])
+def test_balanced_mode_piece_slots(lens, Hkv, C):
+    """Host mirror of the balanced mode's bookkeeping: every tile lies in exactly one chunk,
+    pieces (chunk x segment) get unique slots below C + Hkv*B, and the non-empty chunks of
+    the merge's chunk range for each segment are exactly the chunks that hold its tiles
+    (with fewer tiles than chunks, empty chunks sit inside that range)."""
+    B = len(lens)
+    nt = [-(-L // 16) for L in lens]
+    pre = [0]
+    for n in nt:
+        pre.append(pre[-1] + n)
+    T = Hkv * pre[-1]
+    seen_slots = set()
+    owner = {}
+    for ch in range(C):
+        tb, te = T * ch // C, T * (ch + 1) // C
+        assert te - tb <= max(1, -(-T // C))
+        for t in range(tb, te):
+            g, rem = divmod(t, pre[-1])
+            b = max(i for i in range(B) if pre[i] <= rem)
+            assert chunk_of(t, T, C) == ch
+            owner.setdefault((g, b), set()).add(ch)
+            seen_slots.add(ch + g * B + b)
+    assert all(s < C + Hkv * B for s in seen_slots)
+    assert len(seen_slots) == sum(len(v) for v in owner.values())
+    for (g, b), chunks in owner.items():
+        s0 = g * pre[-1] + pre[b]
+        c0, c1 = chunk_of(s0, T, C), chunk_of(s0 + nt[b] - 1, T, C)
+        live = {c for c in range(c0, c1 + 1) if T * c // C != T * (c + 1) // C}
+        assert chunks == live   # the merge reads exactly these pieces
 
 
 def test_mla_rejects_bad_arguments_before_launch(lib):
