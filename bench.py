@@ -32,17 +32,21 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode attn: KV GB/s read & % of MI355X HBM peak; decode tokens/s"
 HBM_PEAK_GBS = 8000.0                       # MI355X HBM3E, 8 TB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["paged_kv_cache_288_amd/csrc/gqa_decode.hip",
-                  "paged_kv_cache_288_amd/csrc/pkv_device.hpp"]
+KERNEL_SOURCES = {
+    "gqa": ["paged_kv_cache_288_amd/csrc/gqa_stream.hip", "paged_kv_cache_288_amd/csrc/gqa_decode.hip",
+            "paged_kv_cache_288_amd/csrc/gqa_tile.hpp", "paged_kv_cache_288_amd/csrc/pkv_device.hpp"],
+    "mla": ["paged_kv_cache_288_amd/csrc/mla_decode.hip", "paged_kv_cache_288_amd/csrc/gqa_decode.hip",
+            "paged_kv_cache_288_amd/csrc/pkv_device.hpp"],
+}
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_hash():
+def kernel_hash(kind):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -58,7 +62,7 @@ def kv_bytes(w):
     return int(w.context_lens.astype(np.int64).sum()) * per_token
 
 
-def traffic_for(workload_name):
+def traffic_for(workload_name, kind):
     """Measured HBM bytes per call from committed counter runs, if they were taken on
     the current kernel source; otherwise None."""
     try:
@@ -67,9 +71,17 @@ def traffic_for(workload_name):
     except (OSError, ValueError):
         return None
     e = t.get(workload_name)
-    if not e or e.get("kernel_hash") != kernel_hash():
+    if not e or e.get("kernel_hash") != kernel_hash(kind):
         return None
     return e.get("bytes_per_call")
+
+
+def kernel_label(w, pkv, ps):
+    if w.kind == "mla":
+        return "pkv_paged_decode_attn_mla call (mla_decode_kernel + partition_merge_kernel<512>)"
+    if pkv.decode_partition_size(w.B, w.Hkv, w.max_context_len, ps) == 0:
+        return "pkv_paged_decode_attn call, balanced mode (gqa_stream_kernel + stream_merge_kernel)"
+    return "pkv_paged_decode_attn call, partitioned (gqa_decode_kernel + partition_merge_kernel)"
 
 
 def cpu_baseline(w, target_s=15.0):
@@ -252,9 +264,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic_for(w.name),
-            "kernel": "pkv_paged_decode_attn call (gqa_decode_kernel + partition_merge_kernel)"
-            if w.kind != "mla" else "pkv_paged_decode_attn_mla call",
+            "traffic": traffic_for(w.name, w.kind),
+            "kernel": kernel_label(w, pkv, ps),
             "call_ms_avg": round(call_avg, 5),
             "call_ms_median": round(float(np.median(call_ms)), 5),
             "call_ms_p90": round(float(np.percentile(call_ms, 90)), 5),

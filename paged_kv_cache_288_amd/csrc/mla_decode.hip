@@ -83,7 +83,7 @@ __device__ __forceinline__ float group_sum4(float x) {
 
 }  // namespace
 
-__global__ __launch_bounds__(kWaves * kWave, 1) void mla_decode_kernel(MlaArgs a, int head_groups,
+__global__ __launch_bounds__(kWaves * kWave, 2) void mla_decode_kernel(MlaArgs a, int head_groups,
                                                                         int units) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kKLds + kVtLds];
   uint8_t* ldsK = lds;
@@ -180,16 +180,19 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void mla_decode_kernel(MlaArgs a
 
     // ---- S^T = K Q^T for the stage's two 16-token tiles
     f32x4_t s[2];
-#pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      const uint8_t* krow = ldsK + (tile * 16 + c16) * kKStride + 16 * g;
+    s[0] = s[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    {
+      const uint8_t* krow0 = ldsK + c16 * kKStride + 16 * g;
+      const uint8_t* krow1 = krow0 + 16 * kKStride;
 #pragma unroll
       for (int ks = 0; ks < kDqk / 32; ++ks) {
-        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, *(const uint4*)(krow + ks * 64));
-        acc = mfma(kf, qf[ks], acc);
+        const bf16x8_t k0 = __builtin_bit_cast(bf16x8_t, *(const uint4*)(krow0 + ks * 64));
+        const bf16x8_t k1 = __builtin_bit_cast(bf16x8_t, *(const uint4*)(krow1 + ks * 64));
+        s[0] = mfma(k0, qf[ks], s[0]);
+        s[1] = mfma(k1, qf[ks], s[1]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // then 2 MFMA
       }
-      s[tile] = acc;
     }
 
     // ---- online softmax (log2 domain); lane holds tokens tile*16 + 4g + i of head c16
@@ -236,6 +239,8 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void mla_decode_kernel(MlaArgs a
       const uint2 v1 = *(const uint2*)(vrow + 32 + 8 * g);   // tokens 16+4g..16+4g+3
       const f16x8_t vf = __builtin_bit_cast(f16x8_t, uint4{v0.x, v0.y, v1.x, v1.y});
       o[n] = mfma_h(pf, vf, o[n]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // the next tiles' LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // interleaved with the MFMAs
     }
   }
   if (!active) return;
