@@ -37,7 +37,8 @@ template <int D, int G, bool FP8>
 __global__ __launch_bounds__(kWaves * kWave, 2) void gqa_decode_kernel(DecodeArgs a) {
   using Lo = Layout<D, FP8>;
   const int g = blockIdx.x, part = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int k = lane >> 3, c = lane & 7, r = lane / Lo::LPT, dc = lane % Lo::LPT;
   const int t0 = part * a.partition;
   const int tiles_per_block = a.block_size / kTile;
@@ -87,12 +88,16 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void gqa_decode_kernel(DecodeArg
   const uint8_t* vbase = a.v_pool + (size_t)g * head_bytes;
   const float cscale = a.scale * kLog2e * (FP8 ? a.k_scale[g] : 1.f);
 
-  auto tile_addr = [&](int n, const uint8_t*& kt, const uint8_t*& vt) -> int {
+  // Source of this wave's tile n, or an empty one (all loads return zeros) for n >= nt.
+  auto tile_at = [&](int n, int& nv) -> TileSrc {
+    if (n >= nt) {
+      nv = 0;
+      return tile_src<D, FP8>(kbase, vbase, 0);
+    }
     const uint64_t off = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)off_lo, n) |
                          ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)off_hi, n) << 32);
-    kt = kbase + off;
-    vt = vbase + off;
-    return __builtin_amdgcn_readlane(nv_lane, n);
+    nv = __builtin_amdgcn_readlane(nv_lane, n);
+    return tile_src<D, FP8>(kbase + off, vbase + off, nv);
   };
 
   // Two tile buffers, refilled half by half: a tile's K is replaced by the tile two ahead
@@ -100,44 +105,49 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void gqa_decode_kernel(DecodeArg
   // are always in flight.
   const uint32_t koff = k_lane_offset<D, FP8>(k, c), voff = v_lane_offset<D, FP8>(r, dc);
   TileRegs<D, FP8> RA, RB;
-  const uint8_t *ktA, *vtA, *ktB, *vtB;
-  int nvA = 0, nvB = 0;
-  if (nt > 0) {
-    nvA = tile_addr(0, ktA, vtA);
-    load_k<D, FP8>(RA, ktA, koff);
-    load_v<D, FP8>(RA, vtA, voff);
-  }
-  if (nt > 1) {
-    nvB = tile_addr(1, ktB, vtB);
-    load_k<D, FP8>(RB, ktB, koff);
-    load_v<D, FP8>(RB, vtB, voff);
-  }
-  for (int n = 0; n < nt; n += 2) {
+  int nvA, nvB;
+  TileSrc A = tile_at(0, nvA), Bt = tile_at(1, nvB);
+  // issued in this order (the scheduling fences keep it), so the loop's waits are counts of
+  // the loads issued after the data it needs
+  load_k<D, FP8>(RA, A.k, koff);
+  sched_fence();
+  load_v<D, FP8>(RA, A.v, voff);
+  sched_fence();
+  load_k<D, FP8>(RB, Bt.k, koff);
+  sched_fence();
+  load_v<D, FP8>(RB, Bt.v, voff);
+  sched_fence();
+  // Pairs of tiles, then a last single tile: no exit from the middle of the loop, so every
+  // path around it issues the same loads and its waits stay exact.
+  int n = 0;
+  for (; n + 1 < nt; n += 2) {
     {
       uint32_t pairs[Lo::NPS];
       qk_softmax<D, G, FP8>(S, RA, nvA, cscale, lane, pairs);
-      int nv_next = 0;
-      if (n + 2 < nt) {
-        nv_next = tile_addr(n + 2, ktA, vtA);
-        load_k<D, FP8>(RA, ktA, koff);
-      }
-      pv_accumulate<D, G, FP8>(S, RA, nvA, lane, pairs);
-      if (n + 2 < nt) load_v<D, FP8>(RA, vtA, voff);
-      nvA = nv_next;
+      sched_fence();
+      A = tile_at(n + 2, nvA);
+      load_k<D, FP8>(RA, A.k, koff);
+      sched_fence();
+      pv_accumulate<D, G, FP8>(S, RA, lane, pairs);
+      sched_fence();
+      load_v<D, FP8>(RA, A.v, voff);
     }
-    if (n + 1 >= nt) break;
     {
       uint32_t pairs[Lo::NPS];
       qk_softmax<D, G, FP8>(S, RB, nvB, cscale, lane, pairs);
-      int nv_next = 0;
-      if (n + 3 < nt) {
-        nv_next = tile_addr(n + 3, ktB, vtB);
-        load_k<D, FP8>(RB, ktB, koff);
-      }
-      pv_accumulate<D, G, FP8>(S, RB, nvB, lane, pairs);
-      if (n + 3 < nt) load_v<D, FP8>(RB, vtB, voff);
-      nvB = nv_next;
+      sched_fence();
+      Bt = tile_at(n + 3, nvB);
+      load_k<D, FP8>(RB, Bt.k, koff);
+      sched_fence();
+      pv_accumulate<D, G, FP8>(S, RB, lane, pairs);
+      sched_fence();
+      load_v<D, FP8>(RB, Bt.v, voff);
     }
+  }
+  if (n < nt) {
+    uint32_t pairs[Lo::NPS];
+    qk_softmax<D, G, FP8>(S, RA, nvA, cscale, lane, pairs);
+    pv_accumulate<D, G, FP8>(S, RA, lane, pairs);
   }
 
   // ---- merge the wave's row groups: every lane ends with the wave's state for its dims

@@ -33,7 +33,10 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void gqa_stream_kernel(DecodeArg
   using Lo = Layout<D, FP8>;
   __shared__ int s_pre[kMaxStreamSeqs + 1];
   __shared__ int s_sum[kWaves * kWave];
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  // w and everything derived from it are wave-uniform: readfirstlane tells the compiler so,
+  // which keeps the per-tile buffer resources in scalar registers
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int k = lane >> 3, c = lane & 7, r = lane / Lo::LPT, dc = lane % Lo::LPT;
   const int B = a.B;
   const int cap = a.max_blocks * a.block_size;
@@ -70,7 +73,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void gqa_stream_kernel(DecodeArg
     for (int i = tid; i <= B; i += kWaves * kWave) a.ws_prefix[i] = s_pre[i];
 
   // ---- this wave's chunk
-  const int T_head = s_pre[B];
+  const int T_head = __builtin_amdgcn_readfirstlane(s_pre[B]);
   const long long T = (long long)a.Hkv * T_head;
   const int C = a.chunks;
   const int ch = (blockIdx.x & 7) * (C / 8) + (blockIdx.x >> 3) * kWaves + w;
@@ -111,13 +114,17 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void gqa_stream_kernel(DecodeArg
     }
   }
   auto pick = [](int j, int x0, int x1) { return j ? x1 : x0; };
-  auto tile_addr = [&](int n, const uint8_t*& kt, const uint8_t*& vt) -> int {
+  // Source of chunk tile n, or an empty one (all loads return zeros) for n >= end.
+  auto tile_at = [&](int n, int end, int& nv) -> TileSrc {
+    if (n >= end) {
+      nv = 0;
+      return tile_src<D, FP8>(a.k_pool, a.v_pool, 0);
+    }
     const int j = n >> 6, ln = n & (kWave - 1);
     const uint64_t off =
         (uint64_t)(uint32_t)__builtin_amdgcn_readlane(pick(j, (int)off_l[0], (int)off_l[1]), ln) << 8;
-    kt = a.k_pool + off;
-    vt = a.v_pool + off;
-    return __builtin_amdgcn_readlane(pick(j, info_l[0], info_l[1]), ln) & 31;
+    nv = __builtin_amdgcn_readlane(pick(j, info_l[0], info_l[1]), ln) & 31;
+    return tile_src<D, FP8>(a.k_pool + off, a.v_pool + off, nv);
   };
   auto tile_seg = [&](int n) {
     return __builtin_amdgcn_readlane(pick(n >> 6, info_l[0], info_l[1]), n & (kWave - 1)) >> 5;
@@ -154,41 +161,51 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void gqa_stream_kernel(DecodeArg
     const float cscale = a.scale * kLog2e * (FP8 ? a.k_scale[gg] : 1.f);
     const float vs = FP8 ? a.v_scale[gg] : 1.f;
 
-    const uint8_t *ktA, *vtA, *ktB, *vtB;
-    int nvA = tile_addr(n0, ktA, vtA), nvB = 0;
-    load_k<D, FP8>(RA, ktA, koff);
-    load_v<D, FP8>(RA, vtA, voff);
-    if (n0 + 1 < n1) {
-      nvB = tile_addr(n0 + 1, ktB, vtB);
-      load_k<D, FP8>(RB, ktB, koff);
-      load_v<D, FP8>(RB, vtB, voff);
-    }
-    for (int n = n0; n < n1; n += 2) {
+    // Two tile buffers, refilled half by half: a tile's K is replaced by the tile two
+    // ahead as soon as its scores are done, its V once p.V is done.
+    int nvA, nvB;
+    TileSrc A = tile_at(n0, n1, nvA), Bt = tile_at(n0 + 1, n1, nvB);
+    // issued in this order (the scheduling fences keep it), so the loop's waits are counts of
+    // the loads issued after the data it needs
+    load_k<D, FP8>(RA, A.k, koff);
+    sched_fence();
+    load_v<D, FP8>(RA, A.v, voff);
+    sched_fence();
+    load_k<D, FP8>(RB, Bt.k, koff);
+    sched_fence();
+    load_v<D, FP8>(RB, Bt.v, voff);
+    sched_fence();
+    // Pairs of tiles, then a last single tile: no exit from the middle of the loop, so every
+    // path around it issues the same loads and its waits stay exact.
+    int n = n0;
+    for (; n + 1 < n1; n += 2) {
       {
         uint32_t pairs[Lo::NPS];
         qk_softmax<D, G, FP8>(S, RA, nvA, cscale, lane, pairs);
-        int nv_next = 0;
-        if (n + 2 < n1) {
-          nv_next = tile_addr(n + 2, ktA, vtA);
-          load_k<D, FP8>(RA, ktA, koff);
-        }
-        pv_accumulate<D, G, FP8>(S, RA, nvA, lane, pairs);
-        if (n + 2 < n1) load_v<D, FP8>(RA, vtA, voff);
-        nvA = nv_next;
+        sched_fence();
+        A = tile_at(n + 2, n1, nvA);
+        load_k<D, FP8>(RA, A.k, koff);
+        sched_fence();
+        pv_accumulate<D, G, FP8>(S, RA, lane, pairs);
+        sched_fence();
+        load_v<D, FP8>(RA, A.v, voff);
       }
-      if (n + 1 >= n1) break;
       {
         uint32_t pairs[Lo::NPS];
         qk_softmax<D, G, FP8>(S, RB, nvB, cscale, lane, pairs);
-        int nv_next = 0;
-        if (n + 3 < n1) {
-          nv_next = tile_addr(n + 3, ktB, vtB);
-          load_k<D, FP8>(RB, ktB, koff);
-        }
-        pv_accumulate<D, G, FP8>(S, RB, nvB, lane, pairs);
-        if (n + 3 < n1) load_v<D, FP8>(RB, vtB, voff);
-        nvB = nv_next;
+        sched_fence();
+        Bt = tile_at(n + 3, n1, nvB);
+        load_k<D, FP8>(RB, Bt.k, koff);
+        sched_fence();
+        pv_accumulate<D, G, FP8>(S, RB, lane, pairs);
+        sched_fence();
+        load_v<D, FP8>(RB, Bt.v, voff);
       }
+    }
+    if (n < n1) {
+      uint32_t pairs[Lo::NPS];
+      qk_softmax<D, G, FP8>(S, RA, nvA, cscale, lane, pairs);
+      pv_accumulate<D, G, FP8>(S, RA, lane, pairs);
     }
 
     GroupStats<G> X;

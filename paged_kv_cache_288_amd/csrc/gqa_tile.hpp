@@ -45,37 +45,48 @@ __device__ __forceinline__ int pv_token(int u, int r) {
   else return 8 * u + r;
 }
 
-// Value of lane "head h of this lane's p.V group" (see layouts above) in every lane.
+// After the q.K reduction (reduce8 below) lane c of a token's 8 lanes holds head
+// head_of_lane<G>(c); lane_of_head(H) is a lane that holds head H.  The map is c with bits
+// 0-1 flipped when bit 2 is set: it makes each DPP step's partner (lanes c^7, c^2, c^1)
+// hold, at the same register index, the head this lane keeps.
+template <int G>
+__device__ __forceinline__ int head_of_lane(int c) {
+  return ((c & 4) ? c ^ 3 : c) & (G - 1);
+}
+constexpr int lane_of_head(int H) { return (H & 4) ? H ^ 3 : H; }
+
+// Value that the lane holding head H in this lane's p.V group has, in every lane.
 template <int D, int H>
 __device__ __forceinline__ float group_bcast(float x, int lane) {
+  constexpr int LH = lane_of_head(H);
   if constexpr (D == 128) {
-    return row_bcast<H>(x);
+    return row_bcast<LH>(x);
   } else {
-    float lo = row_bcast<H>(x), hi = row_bcast<8 + H>(x);
+    float lo = row_bcast<LH>(x), hi = row_bcast<8 + LH>(x);
     return (lane & 8) ? hi : lo;
   }
 }
 template <int D, int H>
 __device__ __forceinline__ uint32_t group_bcast_u(uint32_t x, int lane) {
+  constexpr int LH = lane_of_head(H);
   if constexpr (D == 128) {
-    return row_bcast_u<H>(x);
+    return row_bcast_u<LH>(x);
   } else {
-    uint32_t lo = row_bcast_u<H>(x), hi = row_bcast_u<8 + H>(x);
+    uint32_t lo = row_bcast_u<LH>(x), hi = row_bcast_u<8 + LH>(x);
     return (lane & 8) ? hi : lo;
   }
 }
 
-// Sum over the 8 lanes of a q.K token of x[0..G-1]; lane c receives head c & (G-1).
-// Steps over lane bits 2, 1, 0; a step halves the value count (reduce-scatter) while more
-// values than remaining steps' capacity are left, otherwise it is a plain all-reduce.
+// Sum over the 8 lanes of a q.K token of x[0..G-1], where lane c holds head
+// j ^ head_of_lane<G>(c) in x[j] (q is loaded in that order); lane c receives head
+// head_of_lane<G>(c) in x[0].  Steps over the partners c^7, c^2, c^1; while more values are
+// left than the remaining steps can separate, a step all-reduces, otherwise it
+// reduce-scatters: x[i] += partner's x[i + N/2], which by the head order above is the same
+// head, so no lane-dependent selection is needed.
 template <int N, int CTRL>
-__device__ __forceinline__ void rs_step(float* x, bool upper) {
+__device__ __forceinline__ void rs_step(float* x) {
 #pragma unroll
-  for (int i = 0; i < N / 2; ++i) {
-    float keep = upper ? x[i + N / 2] : x[i];
-    float send = upper ? x[i] : x[i + N / 2];
-    x[i] = keep + dpp<CTRL>(send);
-  }
+  for (int i = 0; i < N / 2; ++i) x[i] += dpp<CTRL>(x[i + N / 2]);
 }
 template <int N, int CTRL>
 __device__ __forceinline__ void ar_step(float* x) {
@@ -83,19 +94,19 @@ __device__ __forceinline__ void ar_step(float* x) {
   for (int i = 0; i < N; ++i) x[i] += dpp<CTRL>(x[i]);
 }
 template <int G>
-__device__ __forceinline__ float reduce8(float* x, int c) {
+__device__ __forceinline__ float reduce8(float* x) {
   if constexpr (G == 8) {
-    rs_step<8, kDppHalfMirror>(x, c & 4);
-    rs_step<4, kDppQuadXor2>(x, c & 2);
-    rs_step<2, kDppQuadXor1>(x, c & 1);
+    rs_step<8, kDppHalfMirror>(x);
+    rs_step<4, kDppQuadXor2>(x);
+    rs_step<2, kDppQuadXor1>(x);
   } else if constexpr (G == 4) {
     ar_step<4, kDppHalfMirror>(x);
-    rs_step<4, kDppQuadXor2>(x, c & 2);
-    rs_step<2, kDppQuadXor1>(x, c & 1);
+    rs_step<4, kDppQuadXor2>(x);
+    rs_step<2, kDppQuadXor1>(x);
   } else if constexpr (G == 2) {
     ar_step<2, kDppHalfMirror>(x);
     ar_step<2, kDppQuadXor2>(x);
-    rs_step<2, kDppQuadXor1>(x, c & 1);
+    rs_step<2, kDppQuadXor1>(x);
   } else {
     ar_step<1, kDppHalfMirror>(x);
     ar_step<1, kDppQuadXor2>(x);
@@ -108,25 +119,39 @@ template <int D, int G, bool FP8>
 struct WaveState {
   uint32_t q[G][Layout<D, FP8>::NP];  // bf16 pairs of the G query heads, this lane's dims
   float o[G][8];                      // p.V accumulators of this lane's row group
-  float m;                            // running max (log2 domain), head c, this group
-  float l;                            // running sum of probabilities, head c, this group
+  float m;                            // running max (log2 domain), this lane's head, this group
+  float l;                            // running sum of probabilities, same head and group
 };
 
-// K and V of a tile are streamed once and never re-read: nontemporal loads keep them from
-// displacing q, block-table and partial data in the caches.
-__device__ __forceinline__ uint4 load_nt16(const uint8_t* p) {
-  typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
-  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+// ---- K/V tile sources.  A tile's K and V rows are read through buffer resources whose
+// range is the tile's valid rows: rows past it (a sequence's last, partial tile, a block id
+// outside the pool, a tile past the end of a walk) load as zeros without a memory access.
+// So every load is unconditional, and padding never reaches p.V.  K and V are streamed once
+// and never re-read: the loads are nontemporal, which keeps them from displacing q,
+// block-table and partial data in the caches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 resource word 3: raw 32-bit data
+constexpr int kLoadNontemporal = 2;          // cache-policy operand: nt
+
+struct TileSrc {
+  rsrc_t k, v;
+};
+template <int D, bool FP8>
+__device__ __forceinline__ TileSrc tile_src(const uint8_t* kt, const uint8_t* vt, int nv) {
+  const int bytes = nv * Layout<D, FP8>::ROW;
+  return TileSrc{__builtin_amdgcn_make_buffer_rsrc((void*)kt, (short)0, bytes, kRawBufferWord3),
+                 __builtin_amdgcn_make_buffer_rsrc((void*)vt, (short)0, bytes, kRawBufferWord3)};
+}
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadNontemporal);
   return uint4{v[0], v[1], v[2], v[3]};
 }
-__device__ __forceinline__ uint2 load_nt8(const uint8_t* p) {
-  typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
-  const u32x2 v = __builtin_nontemporal_load((const u32x2*)p);
+__device__ __forceinline__ uint2 buf_load8(rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kLoadNontemporal);
   return uint2{v[0], v[1]};
 }
 
-// Per-lane byte offsets inside a tile, constant for the whole walk: with the tile base
-// uniform, every K/V load is "SGPR base + this VGPR + immediate".
+// Per-lane byte offsets inside a tile, constant for the whole walk.
 template <int D, bool FP8>
 __device__ __forceinline__ uint32_t k_lane_offset(int k, int c) {
   return (uint32_t)(k * Layout<D, FP8>::ROW + 16 * c);
@@ -137,24 +162,22 @@ __device__ __forceinline__ uint32_t v_lane_offset(int r, int dc) {
 }
 
 template <int D, bool FP8>
-__device__ __forceinline__ void load_k(TileRegs<D, FP8>& R, const uint8_t* kt, uint32_t koff) {
+__device__ __forceinline__ void load_k(TileRegs<D, FP8>& R, rsrc_t src, uint32_t koff) {
   using Lo = Layout<D, FP8>;
-  const uint8_t* p = kt + koff;
 #pragma unroll
   for (int pi = 0; pi < 2; ++pi)
 #pragma unroll
-    for (int j = 0; j < Lo::KL; ++j) R.k[pi][j] = load_nt16(p + 8 * pi * Lo::ROW + j * 128);
+    for (int j = 0; j < Lo::KL; ++j) R.k[pi][j] = buf_load16(src, koff + 8 * pi * Lo::ROW + j * 128);
 }
 template <int D, bool FP8>
-__device__ __forceinline__ void load_v(TileRegs<D, FP8>& R, const uint8_t* vt, uint32_t voff) {
+__device__ __forceinline__ void load_v(TileRegs<D, FP8>& R, rsrc_t src, uint32_t voff) {
   using Lo = Layout<D, FP8>;
-  const uint8_t* p = vt + voff;
 #pragma unroll
   for (int u = 0; u < Lo::TPG; ++u) {
     // token of slot u minus token of slot 0 does not depend on the row group
-    const uint8_t* q = p + (pv_token<D>(u, 0) - pv_token<D>(0, 0)) * Lo::ROW;
-    if constexpr (FP8) R.v[u] = load_nt8(q);
-    else R.v[u] = load_nt16(q);
+    const uint32_t o = voff + (pv_token<D>(u, 0) - pv_token<D>(0, 0)) * Lo::ROW;
+    if constexpr (FP8) R.v[u] = buf_load8(src, o);
+    else R.v[u] = buf_load16(src, o);
   }
 }
 
@@ -186,7 +209,7 @@ __device__ __forceinline__ void pv_all(WaveState<D, G, FP8>& S, uint32_t pair,
 }
 
 // First half of a 16-token tile: scores and the online-softmax update; returns the
-// probabilities as bf16 token pairs (in `pairs`).  Consumes only R.k, so the caller can
+// probabilities as fp16 token pairs (in `pairs`).  Consumes only R.k, so the caller can
 // refill R.k before the second half.  nv = valid tokens in the tile (16 except a
 // sequence's last tile).
 template <int D, int G, bool FP8>
@@ -194,11 +217,11 @@ __device__ __forceinline__ void qk_softmax(WaveState<D, G, FP8>& S, const TileRe
                                            int nv, float cscale, int lane,
                                            uint32_t (&pairs)[Layout<D, FP8>::NPS]) {
   using Lo = Layout<D, FP8>;
-  const int k = lane >> 3, c = lane & 7;
+  const int k = lane >> 3;
   const bool partial = nv < kTile;
   constexpr auto heads = std::make_integer_sequence<int, G>{};
 
-  // ---- scores for tokens 8*pi + k, head c of this lane
+  // ---- scores for tokens 8*pi + k, head head_of_lane(c) of this lane
   float s[2];
 #pragma unroll
   for (int pi = 0; pi < 2; ++pi) {
@@ -222,17 +245,17 @@ __device__ __forceinline__ void qk_softmax(WaveState<D, G, FP8>& S, const TileRe
     float acc[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float a = 0.f;
+      float a = dot2_zero(S.q[h][0], kp[0]);
 #pragma unroll
-      for (int p = 0; p < Lo::NP; ++p) a = dot2(S.q[h][p], kp[p], a);
+      for (int p = 1; p < Lo::NP; ++p) a = dot2(S.q[h][p], kp[p], a);
       acc[h] = a;
     }
-    float sc = reduce8<G>(acc, c) * cscale;
+    float sc = reduce8<G>(acc) * cscale;
     if (partial && (8 * pi + k) >= nv) sc = kNegInf;
     s[pi] = sc;
   }
 
-  // ---- running max of this group for head c; lazy rescale
+  // ---- running max of this group for the lane's head; lazy rescale
   float mt = fmaxf(s[0], s[1]);
   if constexpr (D == 128) mt = fmaxf(mt, dpp<kDppRowRor8>(mt));
   if (wave_any(mt > S.m + kRescaleSlack)) {
@@ -260,19 +283,14 @@ __device__ __forceinline__ void qk_softmax(WaveState<D, G, FP8>& S, const TileRe
 
 }
 
-// Second half of a tile: p.V accumulation.  Consumes only R.v.
+// Second half of a tile: p.V accumulation.  Consumes only R.v (rows past the tile's valid
+// tokens were loaded as zeros and carry zero probability).
 template <int D, int G, bool FP8>
-__device__ __forceinline__ void pv_accumulate(WaveState<D, G, FP8>& S, TileRegs<D, FP8>& R,
-                                              int nv, int lane,
+__device__ __forceinline__ void pv_accumulate(WaveState<D, G, FP8>& S, const TileRegs<D, FP8>& R,
+                                              int lane,
                                               const uint32_t (&pairs)[Layout<D, FP8>::NPS]) {
   using Lo = Layout<D, FP8>;
-  const int r = lane / Lo::LPT;
   constexpr auto heads = std::make_integer_sequence<int, G>{};
-  if (nv < kTile) {
-#pragma unroll
-    for (int u = 0; u < Lo::TPG; ++u)
-      if (pv_token<D>(u, r) >= nv) R.v[u] = typename VReg<FP8>::T{};
-  }
 #pragma unroll
   for (int j = 0; j < Lo::NPS; ++j) {
     uint32_t vp[8];
@@ -360,13 +378,15 @@ __device__ __forceinline__ void wave_merge_rows(GroupStats<G>& X, WaveState<D, G
 }
 
 // q pairs of the G heads starting at qg ([G][D] bf16) for this lane's dims (the same dims
-// as its K pieces); clears the accumulators.
+// as its K pieces), S.q[j] holding head j ^ head_of_lane<G>(c) (the order reduce8 needs);
+// clears the accumulators.
 template <int D, int G, bool FP8>
 __device__ __forceinline__ void load_q_reset(WaveState<D, G, FP8>& S, const uint16_t* qg, int c) {
   using Lo = Layout<D, FP8>;
+  const int hm = head_of_lane<G>(c);
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const uint8_t* qh = (const uint8_t*)(qg + (size_t)h * D);
+    const uint8_t* qh = (const uint8_t*)(qg + (size_t)(h ^ hm) * D);
     if constexpr (FP8) {
       const uint4 x0 = *(const uint4*)(qh + 32 * c), x1 = *(const uint4*)(qh + 32 * c + 16);
       const uint32_t v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};

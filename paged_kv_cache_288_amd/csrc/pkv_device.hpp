@@ -59,6 +59,13 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
+// dot2(a, b, 0) in the three-operand encoding, whose accumulator can be the constant 0
+// (the two-operand form accumulates in place and would need a zeroed register).
+__device__ __forceinline__ float dot2_zero(uint32_t a, uint32_t b) {
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c,
                                 false);
@@ -95,6 +102,9 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;   // (1.0, 1.0) in bf16
 constexpr uint32_t kOnesF16x2 = 0x3C003C00u;    // (1.0, 1.0) in fp16
+
+// Nothing is scheduled across this point (keeps loads where the source puts them).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
