@@ -212,8 +212,8 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // out[b][h] = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p over the sequence's partitions.
-// One wave per (sequence, head): the partitions' statistics are loaded one per lane, their
-// factors broadcast by readlane while the lanes stream the partial outputs.
+// One wave per (sequence, head): the partitions' statistics are loaded one per lane, then
+// the partial outputs are streamed several rows per load (rows_accumulate).
 template <int D>
 __global__ __launch_bounds__(kWave) void partition_merge_kernel(
     const float* __restrict__ ws_m, const float* __restrict__ ws_l,
@@ -235,7 +235,8 @@ __global__ __launch_bounds__(kWave) void partition_merge_kernel(
   for (int p0 = 0; p0 < nP; p0 += kWave)
     if (p0 + lane < nP) M = fmaxf(M, ws_m[base + p0 + lane]);
   M = wave_max(M);
-  float acc[PER] = {};
+  RowAcc<D> acc;
+  rows_clear(acc);
   float den = 0.f;
   for (int p0 = 0; p0 < nP; p0 += kWave) {
     float f = 0.f, lp = 0.f;
@@ -245,17 +246,9 @@ __global__ __launch_bounds__(kWave) void partition_merge_kernel(
       f = (mp == kNegInf) ? 0.f : fast_exp2(mp - M);
     }
     den += wave_sum(f * lp);
-    const int cnt = min(kWave, nP - p0);
-    const float* op = ws_o + (base + p0) * D + lane;
-    for (int j = 0; j < cnt; ++j) {
-      const float fj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j));
-#pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] += fj * op[(size_t)j * D + kWave * i];
-    }
+    rows_accumulate<D>(acc, ws_o + (base + p0) * D, D, f, min(kWave, nP - p0), lane);
   }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) o[lane + kWave * i] = acc[i] * inv;
+  rows_store<D>(acc, o, den > 0.f ? 1.f / den : 0.f, lane);
 }
 
 template <int D, int G, bool FP8>

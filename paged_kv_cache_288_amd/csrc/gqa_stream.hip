@@ -263,7 +263,8 @@ __global__ __launch_bounds__(kWave) void stream_merge_kernel(DecodeArgs a) {
     if (p0 + lane < np && live(p0 + lane)) M = fmaxf(M, a.ws_m[(slot0 + p0 + lane) * G + h]);
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) M = fmaxf(M, __shfl_xor(M, s));
-  float acc[PER] = {};
+  RowAcc<D> acc;
+  rows_clear(acc);
   float den = 0.f;
   for (int p0 = 0; p0 < np; p0 += kWave) {
     float f = 0.f, lp = 0.f;
@@ -277,18 +278,11 @@ __global__ __launch_bounds__(kWave) void stream_merge_kernel(DecodeArgs a) {
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) fl += __shfl_xor(fl, s);
     den += fl;
-    const int cnt = min(kWave, np - p0);
-    for (int j = 0; j < cnt; ++j) {
-      const float fj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j));
-      if (fj == 0.f) continue;  // empty chunk, or a piece with no valid token
-      const float* op = a.ws_o + ((slot0 + p0 + j) * G + h) * D + lane;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] += fj * op[kWave * i];
-    }
+    // zero weights (empty chunks, pieces without a valid token) are skipped
+    rows_accumulate<D>(acc, a.ws_o + ((slot0 + p0) * G + h) * D, (size_t)G * D, f,
+                       min(kWave, np - p0), lane);
   }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) out[lane + kWave * i] = acc[i] * inv;
+  rows_store<D>(acc, out, den > 0.f ? 1.f / den : 0.f, lane);
 }
 
 template <int D, int G, bool FP8>

@@ -409,4 +409,77 @@ __device__ __forceinline__ void load_q_reset(WaveState<D, G, FP8>& S, const uint
   S.l = 0.f;
 }
 
+// ---- merging partial states
+// acc += sum over j < cnt (<= 64) of f_j * row_j, with row_j = base + j * stride floats and
+// f_j held by lane j.  A zero weight skips its row (that row may never have been written).
+// Rows are read as float4: D/4 lanes per row (all 64 lanes, D/256 loads each, for wider
+// rows), so one load instruction covers several rows, and eight instructions are in flight
+// per lane.  Afterwards the lanes of row slot 0 (lane < LPR) hold the sum.
+template <int D>
+struct RowAcc {
+  static constexpr int LPR = D / 4 < kWave ? D / 4 : kWave;  // lanes per row
+  static constexpr int RPW = kWave / LPR;                     // rows per load instruction
+  static constexpr int V4 = D / 4 / LPR;                      // float4 per lane per row
+  float4 v[V4];
+};
+
+template <int D>
+__device__ __forceinline__ void rows_clear(RowAcc<D>& A) {
+#pragma unroll
+  for (int i = 0; i < RowAcc<D>::V4; ++i) A.v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+template <int D>
+__device__ __forceinline__ void rows_accumulate(RowAcc<D>& A, const float* base, size_t stride,
+                                                float f, int cnt, int lane) {
+  using R = RowAcc<D>;
+  constexpr int U = 8;
+  const int sub = lane / R::LPR, col = lane % R::LPR;
+  for (int j0 = 0; j0 < cnt; j0 += R::RPW * U) {
+    float fj[U];
+    float4 x[U][R::V4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * R::RPW + sub;
+      fj[u] = __shfl(f, j & (kWave - 1));
+      if (j >= cnt) fj[u] = 0.f;
+      const float* row = base + (size_t)(j < cnt ? j : 0) * stride;
+#pragma unroll
+      for (int i = 0; i < R::V4; ++i)
+        x[u][i] = fj[u] != 0.f ? *(const float4*)(row + 4 * (col + R::LPR * i))
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < R::V4; ++i) {
+        A.v[i].x += fj[u] * x[u][i].x;
+        A.v[i].y += fj[u] * x[u][i].y;
+        A.v[i].z += fj[u] * x[u][i].z;
+        A.v[i].w += fj[u] * x[u][i].w;
+      }
+  }
+}
+
+// Sums the row slots into slot 0 and writes scale * sum to out[0..D) from lanes < LPR.
+template <int D>
+__device__ __forceinline__ void rows_store(RowAcc<D>& A, float* out, float scale, int lane) {
+  using R = RowAcc<D>;
+#pragma unroll
+  for (int m = R::LPR; m < kWave; m <<= 1)
+#pragma unroll
+    for (int i = 0; i < R::V4; ++i) {
+      A.v[i].x += __shfl_xor(A.v[i].x, m);
+      A.v[i].y += __shfl_xor(A.v[i].y, m);
+      A.v[i].z += __shfl_xor(A.v[i].z, m);
+      A.v[i].w += __shfl_xor(A.v[i].w, m);
+    }
+  if (lane < R::LPR) {
+#pragma unroll
+    for (int i = 0; i < R::V4; ++i)
+      *(float4*)(out + 4 * (lane + R::LPR * i)) =
+          make_float4(A.v[i].x * scale, A.v[i].y * scale, A.v[i].z * scale, A.v[i].w * scale);
+  }
+}
+
 }  // namespace pkv
