@@ -17,7 +17,8 @@ LIB = os.path.join(HERE, "libpkv.so")
 READ_CEILING = os.path.join(HERE, "read_ceiling")   # standalone bandwidth probe
 ARCH = "gfx950"
 
-SOURCES = ["pkv_api.hip", "kv_append.hip", "gqa_decode.hip", "gqa_stream.hip", "mla_decode.hip"]
+SOURCES = ["pkv_api.hip", "kv_append.hip", "gqa_decode.hip", "gqa_stream.hip", "mla_decode.hip",
+           "mla_stream.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -291,8 +291,7 @@ static hipError_t launch_stream_one(const DecodeArgs& a, hipStream_t s) {
                      0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(stream_merge_kernel<D>, dim3((unsigned)a.B * a.Hq), dim3(kWave), 0, s, a);
-  return hipGetLastError();
+  return launch_stream_merge(a, s);
 }
 
 template <int D, bool FP8>
@@ -304,6 +303,15 @@ static hipError_t launch_stream_d(const DecodeArgs& a, hipStream_t s) {
     case 8: return launch_stream_one<D, 8, FP8>(a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_stream_merge(const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)a.B * a.Hq);
+  if (a.d == 128) hipLaunchKernelGGL(stream_merge_kernel<128>, grid, dim3(kWave), 0, s, a);
+  else if (a.d == 64) hipLaunchKernelGGL(stream_merge_kernel<64>, grid, dim3(kWave), 0, s, a);
+  else if (a.d == 512) hipLaunchKernelGGL(stream_merge_kernel<512>, grid, dim3(kWave), 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_gqa_stream(const DecodeArgs& a, hipStream_t s) {

@@ -129,18 +129,13 @@ struct WaveState {
 // So every load is unconditional, and padding never reaches p.V.  K and V are streamed once
 // and never re-read: the loads are nontemporal, which keeps them from displacing q,
 // block-table and partial data in the caches.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 resource word 3: raw 32-bit data
-constexpr int kLoadNontemporal = 2;          // cache-policy operand: nt
-
 struct TileSrc {
   rsrc_t k, v;
 };
 template <int D, bool FP8>
 __device__ __forceinline__ TileSrc tile_src(const uint8_t* kt, const uint8_t* vt, int nv) {
   const int bytes = nv * Layout<D, FP8>::ROW;
-  return TileSrc{__builtin_amdgcn_make_buffer_rsrc((void*)kt, (short)0, bytes, kRawBufferWord3),
-                 __builtin_amdgcn_make_buffer_rsrc((void*)vt, (short)0, bytes, kRawBufferWord3)};
+  return TileSrc{make_rsrc(kt, bytes), make_rsrc(vt, bytes)};
 }
 __device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadNontemporal);

@@ -1,0 +1,467 @@
+// Balanced latent (MLA) decode attention on gfx950 (the library's default MLA mode).
+//
+// Same arithmetic as mla_decode.hip: every token caches one latent row C_t of 576 dims
+// (512 latent + 64 RoPE) that all query heads attend to, the whole row as key and its first
+// 512 dims as value ("深入LLM推理：从KV Cache到PD分离的Serving全景解析", section
+// "KV Cache：Transformer的循环状态"; "GPU推理深度拆解：KV Cache视角", "KV Cache 大小与分配演进"):
+//     out[b][h] = softmax_t(scale * q[b][h] . C_t) C_t[0:512].
+// Scores run on the bf16 MFMA, p.V on the fp16 MFMA (weights and value dims in fp16, fp32
+// accumulate), with the lazy online softmax of the other kernels.
+//
+// Division of work.  Each sequence's context is cut into stages of 32 tokens (half a
+// 64-token block, one contiguous 36 KiB run of the pool).  The stages of all sequences are
+// laid end to end and the resulting space is cut into `chunks` equal ranges; a workgroup
+// takes one range for one group of 16*HT query heads, so grid = head groups x chunks and
+// every workgroup gets the same work (+-1 stage).  Where a range meets a sequence it
+// produces a piece: the (m, l, o) state of those tokens for its heads, written to slot
+// chunk + b; the merge kernel (shared with the GQA balanced mode) combines the pieces.  The
+// head groups of one chunk are numbered to land on one XCD, so a stage read from HBM by one
+// of them is found in that XCD's L2 by the others.
+//
+// Per workgroup (4 waves), per stage:
+//  * the stage is copied HBM -> LDS by buffer loads that write LDS directly (no registers),
+//    NBUF - 1 stages ahead; the buffer range is the stage's valid rows, so rows past a
+//    sequence's end (or a block id outside the pool) are never read;
+//  * LDS rows are token-major with the 16-byte chunks of row t XOR-permuted by
+//    (t & 7) ^ ((t >> 3) & 1) within groups of 8, which makes both read patterns below free
+//    of bank conflicts;
+//  * scores: S^T = K Q^T on v_mfma_f32_16x16x32_bf16, K as the A operand read straight from
+//    the token-major rows, Q (B operand) held in registers.  A wave owns one 16-head tile and
+//    2 / (4 / HT) of the stage's two 16-token tiles; waves sharing a head tile exchange
+//    their tile maxima through LDS;
+//  * probabilities P = 2^(s - m) are rounded to fp16 and stored [head][token] in LDS;
+//  * p.V: O += P V on v_mfma_f32_16x16x32_f16.  A wave owns 128 of the 512 output dims for
+//    all heads of the group.  The B operand (8 tokens of one dim per lane) is read from the
+//    token-major rows with ds_read_b64_tr_b16, which transposes 4x4 blocks of 16-bit values
+//    across lanes, and widened bf16 -> fp16 in registers (exact for |v| < 65504).
+#include "pkv_device.hpp"
+#include "pkv_launch.hpp"
+
+namespace pkv {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+constexpr int kDqk = 576;
+constexpr int kDv = 512;
+constexpr int kBlock = 64;
+constexpr int kStage = 32;                          // tokens per stage
+constexpr int kRow = kDqk * 2;                      // 1152 bytes per latent row
+constexpr int kRowChunks = kRow / 16;               // 72
+constexpr int kStageBytes = kStage * kRow;          // 36864
+constexpr int kMWaves = 4;
+constexpr int kMThreads = kMWaves * kWave;
+constexpr int kDmaPerWave = kStageBytes / (16 * kWave) / kMWaves;  // 9 loads per wave per stage
+constexpr int kMaxMlaSeqs = 4096;
+constexpr int kMaxChunkStages = 128;                // two per lane
+constexpr int kPRow = 80;                           // bytes per head row of P (32 fp16 + pad)
+constexpr float kSlack = 8.0f;
+static_assert(kStageBytes % (16 * kWave * kMWaves) == 0, "stage split");
+
+__device__ __forceinline__ f32x4_t mfma_bf16(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_f16(const f16x8_t& a, const f16x8_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// XOR permutation of the 16-byte chunks inside groups of 8 for LDS row t.
+__device__ __forceinline__ int row_swizzle(int t) { return (t & 7) ^ ((t >> 3) & 1); }
+
+// Byte offset in a stage buffer of chunk p (0..71) of row t.
+__device__ __forceinline__ int chunk_offset(int t, int p) {
+  return 16 * (t * kRowChunks + (p ^ row_swizzle(t)));
+}
+
+// Max / sum over the 4 lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float group_max4(float x) {
+  float lo, hi, e, o;
+  halves_pair32(x, lo, hi);
+  x = fmaxf(lo, hi);
+  rows_pair16(x, e, o);
+  return fmaxf(e, o);
+}
+__device__ __forceinline__ float group_sum4(float x) {
+  float lo, hi, e, o;
+  halves_pair32(x, lo, hi);
+  x = lo + hi;
+  rows_pair16(x, e, o);
+  return e + o;
+}
+
+// Raw buffer resource words over [base, base + bytes) (out-of-range loads return zeros).
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+__device__ __forceinline__ i32x4_t rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  return i32x4_t{(int)(uint32_t)p, (int)((uint32_t)(p >> 32) & 0xFFFFu), (int)bytes, kRawBufferWord3};
+}
+
+// 16 bytes per lane from byte offset voff of the buffer into LDS at lds_base + 16 * lane.
+// Issued as assembly so that the compiler does not make every later LDS read wait for all
+// such copies (it cannot tell the stage buffers apart); the kernel waits for each stage
+// itself with s_waitcnt vmcnt.  The copy reads its LDS address from M0 and its resource from
+// SGPRs; the leading s_nop 4 gives the five wait states that an SGPR written by a VALU
+// instruction (readlane) needs before a vector-memory read, which also covers M0's one.
+__device__ __forceinline__ void lds_copy16(i32x4_t rsrc, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
+               "{m0}"(lds_base)
+               : "memory");
+}
+
+// Two bf16 in one dword -> the same two values as fp16 (exact for |v| < 65504).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t x) {
+  return pack_f16(bf16_lo(x), bf16_hi(x));
+}
+
+}  // namespace
+
+template <int HT, int NBUF>
+__global__ __launch_bounds__(kMThreads, 1) void mla_stream_kernel(MlaArgs a) {
+  constexpr int HPU = 16 * HT;   // heads per workgroup
+  constexpr int WPH = 4 / HT;    // waves per head tile in the score phase
+  constexpr int TT = 2 / WPH;    // token tiles per wave in the score phase
+  static_assert(HT == 2 || HT == 4, "head tiles per workgroup");
+  __shared__ __attribute__((aligned(16))) uint8_t sbuf[NBUF * kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sP[HPU * kPRow];
+  __shared__ __attribute__((aligned(16))) float sMax[2][HPU];
+  __shared__ __attribute__((aligned(16))) float sAlpha[HPU];
+  __shared__ float sL[kMWaves][16];
+  static_assert((kMaxMlaSeqs + 1 + kMThreads) * 4 <= NBUF * kStageBytes, "prefix scratch");
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
+  const int i16 = lane & 15, g = lane >> 4;
+  const int B = a.B, Hq = a.Hq, HG = Hq / HPU, C = a.chunks;
+  const int cap = a.max_blocks * kBlock;
+
+  // ---- stages per sequence and their exclusive prefix (scratch in the stage buffers)
+  int* s_pre = (int*)sbuf;
+  int* s_sum = s_pre + kMaxMlaSeqs + 1;
+  auto nstages = [&](int bi) {
+    int L = a.context_lens[bi];
+    L = L < 0 ? 0 : (L > cap ? cap : L);
+    return (L + kStage - 1) / kStage;
+  };
+  {
+    const int per = (B + kMThreads - 1) / kMThreads;
+    int local = 0;
+    for (int i = 0; i < per; ++i)
+      if (tid * per + i < B) local += nstages(tid * per + i);
+    s_sum[tid] = local;
+    __syncthreads();
+    for (int off = 1; off < kMThreads; off <<= 1) {
+      const int v = tid >= off ? s_sum[tid - off] : 0;
+      __syncthreads();
+      s_sum[tid] += v;
+      __syncthreads();
+    }
+    int run = tid == 0 ? 0 : s_sum[tid - 1];
+    for (int i = 0; i < per; ++i) {
+      const int bi = tid * per + i;
+      if (bi < B) {
+        s_pre[bi] = run;
+        run += nstages(bi);
+      }
+    }
+    if (tid == 0) s_pre[B] = s_sum[kMThreads - 1];
+    __syncthreads();
+    if (blockIdx.x == 0)
+      for (int i = tid; i <= B; i += kMThreads) a.ws_prefix[i] = s_pre[i];
+  }
+
+  // ---- this workgroup's head group and chunk: the HG head groups of chunk ch are
+  // consecutive multiples of 8 apart, i.e. on one XCD under round-robin dispatch
+  const int T = __builtin_amdgcn_readfirstlane(s_pre[B]);
+  const int x = blockIdx.x, xcd = x & 7, kx = x >> 3;
+  const int hg = kx % HG, ch = (kx / HG) * 8 + xcd;
+  const long long tb = (long long)T * ch / C, te = (long long)T * (ch + 1) / C;
+  const int ns = (int)min(te - tb, (long long)kMaxChunkStages);
+
+  // ---- per-stage first token (pool row index) and valid-token count | sequence << 6,
+  // two stages per lane
+  uint32_t row_l[2] = {0, 0};
+  int info_l[2] = {0, 0};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = kWave * j + lane;
+    if (n < ns) {
+      const int t = (int)(tb + n);
+      int lo = 0, hi = B - 1;  // last sequence whose first stage is <= t
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_pre[mid] <= t) lo = mid;
+        else hi = mid - 1;
+      }
+      const int js = t - s_pre[lo];
+      int L = a.context_lens[lo];
+      L = L < 0 ? 0 : (L > cap ? cap : L);
+      const int phys = a.block_table[(size_t)lo * a.max_blocks + js / 2];
+      const bool ok = (unsigned)phys < (unsigned)a.num_blocks;
+      row_l[j] = (uint32_t)(ok ? phys : 0) * kBlock + (js & 1) * kStage;
+      info_l[j] = (ok ? min(kStage, L - js * kStage) : 0) | (lo << 6);
+    }
+  }
+  uint64_t starts[2];  // stages that open a new piece
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = kWave * j + lane;
+    const int seq = info_l[j] >> 6;
+    int prev = __shfl_up(seq, 1);
+    if (lane == 0) prev = j ? __builtin_amdgcn_readlane(info_l[0], kWave - 1) >> 6 : -1;
+    starts[j] = __builtin_amdgcn_ballot_w64(n < ns && seq != prev);
+  }
+  auto stage_info = [&](int n) {
+    return __builtin_amdgcn_readlane(n >> 6 ? info_l[1] : info_l[0], n & (kWave - 1));
+  };
+  auto stage_src = [&](int n) -> i32x4_t {
+    if (n >= ns) return rsrc_words(a.kv_pool, 0);
+    const uint32_t row =
+        (uint32_t)__builtin_amdgcn_readlane((int)(n >> 6 ? row_l[1] : row_l[0]), n & (kWave - 1));
+    const int valid = stage_info(n) & 63;
+    return rsrc_words((const uint8_t*)a.kv_pool + (uint64_t)row * kRow, valid * kRow);
+  };
+  auto is_start = [&](int n) { return ((starts[n >> 6] >> (n & (kWave - 1))) & 1ull) != 0; };
+
+  // The prefix scratch is dead from here on; clear the stage buffers once so that rows a
+  // stage does not load hold zeros or earlier valid rows, never garbage.
+  __syncthreads();
+  for (int i = tid; i < NBUF * kStageBytes / 16; i += kMThreads)
+    *(uint4*)(sbuf + 16 * i) = uint4{0, 0, 0, 0};
+  __syncthreads();
+  if (ns <= 0) return;
+
+  // ---- LDS-direct copy of a stage: load j of wave w fills bytes [1024 (9w + j), +1024) of
+  // the buffer; lane -> chunk c = 64 (9w + j) + lane = row t, permuted chunk p'; it loads
+  // chunk p' ^ swizzle(t) of row t from the pool.
+  uint32_t dma_off[kDmaPerWave];
+#pragma unroll
+  for (int j = 0; j < kDmaPerWave; ++j) {
+    const int c = (w * kDmaPerWave + j) * kWave + lane;
+    const int t = c / kRowChunks, pp = c % kRowChunks;
+    dma_off[j] = (uint32_t)(16 * (t * kRowChunks + (pp ^ row_swizzle(t))));
+  }
+  const uint32_t sbuf_lds = (uint32_t)(uintptr_t)(lds_void_t*)sbuf;
+  auto issue_stage = [&](int n) {
+    const i32x4_t src = stage_src(n);
+    const uint32_t base = sbuf_lds + (n % NBUF) * kStageBytes + w * kDmaPerWave * 1024;
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) lds_copy16(src, dma_off[j], base + j * 1024);
+  };
+
+  // ---- score-phase roles and per-lane LDS offsets
+  const int hw = w / WPH;             // head tile of this wave in the score phase
+  const int tt0 = (w % WPH) * TT;     // its first token tile
+  // K (A operand): token tt*16 + i16, chunk 4 ks + g  ->  even / odd ks base offsets
+  int k_off[TT][2];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    const int t = (tt0 + tt) * 16 + i16;
+    const int xm = g ^ row_swizzle(t);
+    k_off[tt][0] = 16 * (t * kRowChunks + xm);
+    k_off[tt][1] = 16 * (t * kRowChunks + (xm ^ 4));
+  }
+  // V (B operand, transposed reads): lane s = i16 reads token 8 g + 4 h + (s >> 2), dims
+  // 128 w + 16 nt + 4 (s & 3) .. +3; the chunk term depends on nt & 3 (plus 8 (nt >> 2))
+  int v_off[2][4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = 8 * g + 4 * h + (i16 >> 2);
+    const int qd = (i16 & 3) >> 1, half8 = 8 * (i16 & 1);
+#pragma unroll
+    for (int n4 = 0; n4 < 4; ++n4)
+      v_off[h][n4] = 16 * (t * kRowChunks + 16 * w + ((2 * n4 + qd) ^ row_swizzle(t))) + half8;
+  }
+
+  // ---- state
+  bf16x8_t qf[kDqk / 32];
+  f32x4_t o[HT][8];
+  float m_run = kNegInf, l_part = 0.f;
+  const float cscale = a.scale * kLog2e;
+  int seq = -1;
+
+  auto flush = [&]() {  // write the finished piece (slot ch + seq) to the workspace
+    const float l_head = group_sum4(l_part);
+    if (g == 0) sL[w][i16] = l_head;
+    barrier_vm<63>();
+    const size_t slot = (size_t)ch + seq;
+    const size_t row0 = slot * Hq + (size_t)hg * HPU;
+    if (tt0 == 0 && g == 0) {
+      float l = 0.f;
+#pragma unroll
+      for (int k2 = 0; k2 < WPH; ++k2) l += sL[hw * WPH + k2][i16];
+      a.ws_m[row0 + hw * 16 + i16] = m_run;
+      a.ws_l[row0 + hw * 16 + i16] = l;
+    }
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          a.ws_o[(row0 + ht * 16 + 4 * g + r) * kDv + 128 * w + 16 * nt + i16] = o[ht][nt][r];
+  };
+
+  for (int n = 0; n < NBUF - 1; ++n) issue_stage(n);
+
+  for (int n = 0; n < ns; ++n) {
+    const int info = stage_info(n);
+    const int valid = info & 63;
+    if (is_start(n)) {
+      if (seq >= 0) flush();
+      seq = info >> 6;
+      const uint8_t* qrow =
+          (const uint8_t*)(a.q + ((size_t)seq * Hq + (size_t)hg * HPU + hw * 16 + i16) * kDqk);
+#pragma unroll
+      for (int ks = 0; ks < kDqk / 32; ++ks)
+        qf[ks] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(qrow + ks * 64 + 16 * g));
+      // Wait for q here, once per piece: otherwise the compiler's count-based waits for q
+      // (which do not know about the stage copies) would drain the copy pipeline at every
+      // stage.
+      wait_vm<0>();
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) o[ht][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      m_run = kNegInf;
+      l_part = 0.f;
+    }
+    // stage n has landed once this wave's loads of it are done (NBUF - 2 newer stages may
+    // still be in flight) and every wave got here, which also means every wave is done
+    // reading the buffer that stage n + NBUF - 1 now overwrites
+    barrier_vm<kDmaPerWave * (NBUF - 2)>();
+    issue_stage(n + NBUF - 1);
+    const uint8_t* buf = sbuf + (n % NBUF) * kStageBytes;
+
+    // ---- S^T = K Q^T for this wave's token tiles and head tile
+    f32x4_t s[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) s[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kDqk / 32; ++ks) {
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        const bf16x8_t kf = __builtin_bit_cast(
+            bf16x8_t, *(const uint4*)(buf + k_off[tt][ks & 1] + 128 * (ks >> 1)));
+        s[tt] = mfma_bf16(kf, qf[ks], s[tt]);
+      }
+    }
+
+    // ---- online softmax (log2 domain); lane holds tokens tt*16 + 4g + r of head i16
+    float sv[TT * 4];
+    float mt = kNegInf;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = (tt0 + tt) * 16 + 4 * g + r;
+        const float v = tok < valid ? s[tt][r] * cscale : kNegInf;
+        sv[tt * 4 + r] = v;
+        mt = fmaxf(mt, v);
+      }
+    mt = group_max4(mt);
+    if constexpr (WPH > 1) {  // the other token tile of this head tile is another wave's
+      if (g == 0) sMax[tt0 / TT][hw * 16 + i16] = mt;
+      barrier_vm<63>();
+      mt = fmaxf(sMax[0][hw * 16 + i16], sMax[1][hw * 16 + i16]);
+    }
+    float alpha = 1.f;
+    if (wave_any(mt > m_run + kSlack)) {
+      const float m_new = fmaxf(m_run, mt);
+      alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+      l_part *= alpha;
+      m_run = m_new;
+    }
+    if (tt0 == 0 && g == 0) sAlpha[hw * 16 + i16] = alpha;
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const uint32_t p01 = pack_f16(fast_exp2(sv[tt * 4 + 0] - m_use), fast_exp2(sv[tt * 4 + 1] - m_use));
+      const uint32_t p23 = pack_f16(fast_exp2(sv[tt * 4 + 2] - m_use), fast_exp2(sv[tt * 4 + 3] - m_use));
+      l_part = dot2h(p01, kOnesF16x2, l_part);
+      l_part = dot2h(p23, kOnesF16x2, l_part);
+      *(uint2*)(sP + (hw * 16 + i16) * kPRow + ((tt0 + tt) * 16 + 4 * g) * 2) = uint2{p01, p23};
+    }
+    barrier_vm<63>();
+
+    // ---- O += P V for dims [128 w, 128 w + 128) of all HPU heads
+    {
+      float4 al[HT];
+      bool any = false;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        al[ht] = *(const float4*)&sAlpha[ht * 16 + 4 * g];
+        any |= al[ht].x != 1.f || al[ht].y != 1.f || al[ht].z != 1.f || al[ht].w != 1.f;
+      }
+      if (wave_any(any)) {
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+          for (int nt = 0; nt < 8; ++nt) {
+            o[ht][nt][0] *= al[ht].x;
+            o[ht][nt][1] *= al[ht].y;
+            o[ht][nt][2] *= al[ht].z;
+            o[ht][nt][3] *= al[ht].w;
+          }
+      }
+    }
+    f16x8_t pf[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+      pf[ht] = __builtin_bit_cast(f16x8_t, *(const uint4*)(sP + (ht * 16 + i16) * kPRow + 16 * g));
+    const lds_char_t* lbuf = (const lds_char_t*)((lds_void_t*)buf);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      uint32_t vw[4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(lbuf + v_off[h][nt & 3] + 128 * (nt >> 2)));
+        const uint2 rr = __builtin_bit_cast(uint2, r);
+        vw[2 * h] = bf16x2_to_f16x2(rr.x);
+        vw[2 * h + 1] = bf16x2_to_f16x2(rr.y);
+      }
+      const f16x8_t vf = __builtin_bit_cast(f16x8_t, uint4{vw[0], vw[1], vw[2], vw[3]});
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) o[ht][nt] = mfma_f16(pf[ht], vf, o[ht][nt]);
+    }
+  }
+  flush();
+  // Copies of stages past the end (empty ranges) may still be in flight: they must land
+  // before this workgroup's LDS can be handed to another one.
+  wait_vm<0>();
+}
+
+int mla_stream_heads_per_group(int Hq) { return (Hq % 32 == 0 && Hq <= 128) ? 32 : 0; }
+
+hipError_t launch_mla_stream(const MlaArgs& a, hipStream_t s) {
+  constexpr int HT = 2, NBUF = 4;
+  if (a.d_qk != kDqk || a.d_v != kDv || a.block_size != kBlock || a.B > kMaxMlaSeqs ||
+      mla_stream_heads_per_group(a.Hq) != 16 * HT || a.chunks % 8)
+    return hipErrorInvalidValue;
+  const int HG = a.Hq / (16 * HT);
+  hipLaunchKernelGGL((mla_stream_kernel<HT, NBUF>), dim3((unsigned)(HG * a.chunks)),
+                     dim3(kMThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  DecodeArgs m{};
+  m.out = a.out;
+  m.ws_m = a.ws_m;
+  m.ws_l = a.ws_l;
+  m.ws_o = a.ws_o;
+  m.B = a.B;
+  m.Hq = a.Hq;
+  m.Hkv = 1;
+  m.d = kDv;
+  m.chunks = a.chunks;
+  m.ws_prefix = a.ws_prefix;
+  return launch_stream_merge(m, s);
+}
+
+}  // namespace pkv

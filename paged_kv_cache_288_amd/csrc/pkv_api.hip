@@ -100,6 +100,22 @@ size_t stream_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t ch
          round256(((size_t)B + 1) * sizeof(int32_t));
 }
 
+// Latent balanced mode: one 4-wave workgroup per CU, Hq / 32 head groups, chunks a
+// multiple of 8 and enough of them that none holds more than 128 stages of 32 tokens.
+int32_t mla_stream_chunks(int32_t B, int32_t Hq, int32_t max_ctx) {
+  const long long hg = Hq / pkv::mla_stream_heads_per_group(Hq);
+  const long long smax = (long long)B * ((max_ctx + 31) / 32);
+  long long c = (device_cus() + hg - 1) / hg;
+  const long long need = (smax + 127) / 128;
+  if (need > c) c = need;
+  c = (c + 7) / 8 * 8;
+  return c > (1LL << 24) ? -1 : (int32_t)c;
+}
+
+bool mla_stream_mode(int32_t B, int32_t Hq, int32_t partition_size) {
+  return partition_size == 0 && B <= kMaxStreamSeqs && pkv::mla_stream_heads_per_group(Hq) > 0;
+}
+
 bool stream_mode(int32_t B, int32_t partition_size) {
   return partition_size == 0 && B <= kMaxStreamSeqs;
 }
@@ -243,6 +259,10 @@ pkv_status pkv_paged_decode_attn(float* out, const void* q, const void* k_pool,
 size_t pkv_mla_workspace_bytes(int32_t B, int32_t Hq, int32_t d_v, int32_t max_context_len,
                                int32_t partition_size) {
   if (B < 0 || Hq <= 0 || d_v <= 0 || max_context_len < 0 || partition_size < 0) return 0;
+  if (mla_stream_mode(B, Hq, partition_size)) {
+    const int32_t chunks = mla_stream_chunks(B, Hq, max_context_len);
+    return chunks < 0 ? 0 : stream_ws_bytes(B, Hq, 1, d_v, chunks);
+  }
   const int32_t ps = partition_size > 0 ? partition_size : mla_auto_partition(B, Hq, max_context_len);
   return ws_bytes(B, Hq, d_v, num_parts(max_context_len, ps));
 }
@@ -268,6 +288,25 @@ pkv_status pkv_paged_decode_attn_mla(float* out, const void* q, const void* kv_p
     return PKV_ERR_ALIGN;
   if (B > kGridYZMax) return PKV_ERR_SHAPE;
   const int32_t ctx = max_context_len;
+  hipStream_t s = (hipStream_t)stream;
+  if (mla_stream_mode(B, Hq, partition_size)) {  // balanced mode
+    const int32_t chunks = mla_stream_chunks(B, Hq, ctx);
+    if (chunks < 0) return PKV_ERR_SHAPE;
+    if (!workspace || workspace_bytes < stream_ws_bytes(B, Hq, 1, d_v, chunks))
+      return PKV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+    const size_t rows = ((size_t)chunks + (size_t)B) * (size_t)Hq;
+    char* base = (char*)workspace;
+    float* ws_m = (float*)base;
+    float* ws_l = (float*)(base + round256(rows * sizeof(float)));
+    float* ws_o = (float*)(base + 2 * round256(rows * sizeof(float)));
+    int32_t* ws_p = (int32_t*)(base + 2 * round256(rows * sizeof(float)) +
+                               round256(rows * d_v * sizeof(float)));
+    pkv::MlaArgs a{out, (const uint16_t*)q, (const uint16_t*)kv_pool, block_table, context_lens,
+                   ws_m, ws_l, ws_o, B, Hq, d_qk, d_v, block_size, num_blocks,
+                   max_blocks_per_seq, ctx, 0, 0, scale, chunks, ws_p};
+    return hip_status(pkv::launch_mla_stream(a, s));
+  }
   const int32_t ps = partition_size > 0 ? partition_size : mla_auto_partition(B, Hq, ctx);
   const int32_t P = num_parts(ctx, ps);
   if (P > kGridYZMax) return PKV_ERR_SHAPE;
@@ -279,8 +318,7 @@ pkv_status pkv_paged_decode_attn_mla(float* out, const void* q, const void* kv_p
   }
   pkv::MlaArgs a{out, (const uint16_t*)q, (const uint16_t*)kv_pool, block_table, context_lens,
                  ws_m, ws_l, ws_o, B, Hq, d_qk, d_v, block_size, num_blocks, max_blocks_per_seq,
-                 ctx, ps, P, scale};
-  hipStream_t s = (hipStream_t)stream;
+                 ctx, ps, P, scale, 0, nullptr};
   pkv_status st = hip_status(pkv::launch_mla_decode(a, s));
   if (st != PKV_OK || P == 1) return st;
   return hip_status(pkv::launch_partition_merge(ws_m, ws_l, ws_o, context_lens, out, B, Hq, d_v,

@@ -103,6 +103,38 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;   // (1.0, 1.0) in bf16
 constexpr uint32_t kOnesF16x2 = 0x3C003C00u;    // (1.0, 1.0) in fp16
 
+// ---------------------------------------------------------------- buffer resources
+// A raw buffer resource over [base, base + bytes): loads at offsets past `bytes` return zeros
+// without a memory access (stores there are dropped).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 resource word 3: raw 32-bit data
+constexpr int kLoadNontemporal = 2;          // cache-policy operand: nt
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRawBufferWord3);
+}
+
+// s_waitcnt with vmcnt <= VM (0..63) only.
+template <int VM>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (15 << 8) | ((VM >> 4) << 14));
+}
+// s_waitcnt with vmcnt <= VM (0..63) and lgkmcnt = 0 (expcnt not waited for).
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | ((VM >> 4) << 14));
+}
+// Workgroup barrier that waits only for this wave's LDS operations and its vector memory
+// operations beyond the newest VM (HIP's __syncthreads also drains every global access).
+template <int VM>
+__device__ __forceinline__ void barrier_vm() {
+  asm volatile("" ::: "memory");
+  wait_vm_lgkm0<VM>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Nothing is scheduled across this point (keeps loads where the source puts them).
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 

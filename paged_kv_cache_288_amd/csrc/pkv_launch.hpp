@@ -43,6 +43,8 @@ struct DecodeArgs {
 hipError_t launch_gqa_decode(const DecodeArgs& a, hipStream_t s);
 // Balanced mode: decode kernel + merge kernel (always both).
 hipError_t launch_gqa_stream(const DecodeArgs& a, hipStream_t s);
+// Merge of balanced-mode pieces for d_v = D (128, 64 or 512); reads a.ws_* and a.ws_prefix.
+hipError_t launch_stream_merge(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_partition_merge(const float* ws_m, const float* ws_l, const float* ws_o,
                                   const int32_t* context_lens, float* out, int32_t B,
                                   int32_t Hq, int32_t d, int32_t partition,
@@ -61,7 +63,15 @@ struct MlaArgs {
   int32_t B, Hq, d_qk, d_v, block_size, num_blocks, max_blocks, max_context_len;
   int32_t partition, num_partitions;
   float scale;
+  // balanced mode: chunks per head group (a multiple of 8) and the per-sequence stage prefix
+  // [B + 1] the decode kernel leaves for the merge kernel
+  int32_t chunks;
+  int32_t* ws_prefix;
 };
 hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t s);
+// Balanced mode: decode kernel + merge kernel.  Heads per workgroup for a given Hq
+// (0 = the balanced mode does not support this Hq).
+int mla_stream_heads_per_group(int Hq);
+hipError_t launch_mla_stream(const MlaArgs& a, hipStream_t s);
 
 }  // namespace pkv

@@ -191,3 +191,25 @@ def test_binding_refuses_to_run_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(pkv, "library_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         pkv.load_library()
+
+
+def _mla_chunks(B, Hq, ctx, cus):
+    hg = Hq // 32
+    c = max(-(-cus // hg), -(-(B * -(-ctx // 32)) // 128))
+    return -(-c // 8) * 8
+
+
+def test_mla_balanced_workspace_size(lib):
+    """Latent balanced mode (partition_size 0, Hq a multiple of 32): pieces (chunks + B) x Hq
+    rows of m, l and o[512], plus the stage prefix; 256 CUs assumed without a GPU."""
+    r256 = lambda x: (x + 255) // 256 * 256
+    for B, Hq, ctx in [(32, 128, 8192), (1, 32, 8192), (200, 64, 100), (5, 96, 1500),
+                       (4, 128, 131072)]:
+        C = _mla_chunks(B, Hq, ctx, 256)
+        assert B * -(-ctx // 32) <= 128 * C            # no range exceeds 128 stages
+        rows = (C + B) * Hq
+        want = 2 * r256(rows * 4) + r256(rows * 512 * 4) + r256((B + 1) * 4)
+        assert lib.pkv_mla_workspace_bytes(B, Hq, 512, ctx, 0) == want
+    # Hq not a multiple of 32 (and explicit partitions) use the partitioned kernel
+    assert lib.pkv_mla_workspace_bytes(2, 48, 512, 8192, 0) > 0
+    assert lib.pkv_mla_workspace_bytes(2, 128, 512, 512, 1024) == 0

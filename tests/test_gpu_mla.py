@@ -63,3 +63,58 @@ def test_mla_empty_sequence_gives_zero():
         got = gpu_decode(torch, w, partition_size=ps)
         assert (got[2] == 0).all()
         assert_close(got, oracle_decode(w), "bf16", f"mla empty sequence, partition {ps}")
+
+
+# ---- balanced mode (partition_size 0, Hq a multiple of 32): stage ranges cut across
+# sequences, pieces merged per sequence
+
+def test_mla_balanced_many_short_sequences():
+    """Many pieces per workgroup range: short contexts, partial 32-token stages, empties."""
+    torch = torch_cuda()
+    w = make_workload("mla", seed=11, B=200, lens=("uniform", 0, 100), heads=(64, 1))
+    log(f"[mla] balanced B=200 lens<=100 (zeros: {int((w.context_lens == 0).sum())})")
+    got = gpu_decode(torch, w, partition_size=0)
+    assert_close(got, oracle_decode(w), "bf16", "mla balanced, 200 short sequences")
+
+
+def test_mla_balanced_one_long_sequence():
+    """One sequence spread over every workgroup range (one piece each)."""
+    torch = torch_cuda()
+    w = make_workload("mla", seed=12, B=1, lens=("fixed", [8192]))
+    log("[mla] balanced B=1 L=8192")
+    got = gpu_decode(torch, w, partition_size=0)
+    assert_close(got, oracle_decode(w), "bf16", "mla balanced, one 8192-token sequence")
+
+
+@pytest.mark.parametrize("hq", [32, 96])
+def test_mla_balanced_head_groups(hq):
+    torch = torch_cuda()
+    w = make_workload("mla", seed=13, B=5, lens=("uniform", 1, 1500), heads=(hq, 1))
+    log(f"[mla] balanced Hq={hq} lens={w.context_lens.tolist()}")
+    assert_close(gpu_decode(torch, w, partition_size=0), oracle_decode(w), "bf16",
+                 f"mla balanced Hq {hq}")
+
+
+def test_mla_balanced_matches_partitioned():
+    torch = torch_cuda()
+    w = make_workload("mla", seed=14, B=6, lens=("uniform", 200, 3000))
+    a = gpu_decode(torch, w, partition_size=0)
+    b = gpu_decode(torch, w, partition_size=1024)
+    ref = oracle_decode(w)
+    assert_close(a, ref, "bf16", "mla balanced")
+    assert_close(b, ref, "bf16", "mla partitioned")
+
+
+def test_mla_balanced_large_latent_values():
+    """Latent values up to ~2e4 (inside fp16's range, which p.V uses): compared in units of
+    4096 so that the absolute bound scales with the data."""
+    torch = torch_cuda()
+    w = make_workload("mla", seed=15, B=3, lens=("uniform", 50, 900))
+    from oracle.paged_attention import bf16_bits_to_f64
+    vals = bf16_bits_to_f64(w.k_pool) * 4096.0
+    w.k_pool = (np.asarray(vals, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    w.q = (np.asarray(bf16_bits_to_f64(w.q) / 4096.0, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    got = gpu_decode(torch, w, partition_size=0)
+    ref = oracle_decode(w)
+    assert np.isfinite(got).all()
+    assert_close(got / 4096.0, ref / 4096.0, "bf16", "mla balanced, large latent values")
