@@ -29,9 +29,14 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags.  The latent balanced kernel keeps its MFMA accumulators in VGPRs:
+# in AGPRs the compiler copies them around the kernel's rare rescale branch at every stage.
+SOURCE_FLAGS = {"mla_stream.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src, isa):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if isa:
         cmd += ["-save-temps=obj"]
     r = subprocess.run(cmd, capture_output=True, text=True, cwd=BUILD)

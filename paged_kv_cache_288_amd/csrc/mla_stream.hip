@@ -227,7 +227,6 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_stream_kernel(MlaArgs a) {
     const int valid = stage_info(n) & 63;
     return rsrc_words((const uint8_t*)a.kv_pool + (uint64_t)row * kRow, valid * kRow);
   };
-  auto is_start = [&](int n) { return ((starts[n >> 6] >> (n & (kWave - 1))) & 1ull) != 0; };
 
   // The prefix scratch is dead from here on; clear the stage buffers once so that rows a
   // stage does not load hold zeros or earlier valid rows, never garbage.
@@ -282,6 +281,10 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_stream_kernel(MlaArgs a) {
   // ---- state
   bf16x8_t qf[kDqk / 32];
   f32x4_t o[HT][8];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) o[ht][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};  // finite for alpha = 0
   float m_run = kNegInf, l_part = 0.f;
   const float cscale = a.scale * kLog2e;
   int seq = -1;
@@ -310,12 +313,20 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_stream_kernel(MlaArgs a) {
 
   for (int n = 0; n < NBUF - 1; ++n) issue_stage(n);
 
-  for (int n = 0; n < ns; ++n) {
-    const int info = stage_info(n);
-    const int valid = info & 63;
-    if (is_start(n)) {
-      if (seq >= 0) flush();
-      seq = info >> 6;
+  // Pieces one after another (the stage copies run on across them); within a piece the
+  // accumulators are touched only by MFMAs.
+  auto next_start = [&](int n) {  // first stage after n that opens a piece (or ns)
+    for (int j = (n + 1) >> 6; j < 2; ++j) {
+      const int lo = (n + 1) - kWave * j;
+      const uint64_t m = lo <= 0 ? starts[j] : (lo >= kWave ? 0 : starts[j] & (~0ull << lo));
+      if (m) return kWave * j + (int)__builtin_ctzll(m);
+    }
+    return ns;
+  };
+  for (int n = 0; n < ns;) {
+    const int n_end = next_start(n);
+    seq = stage_info(n) >> 6;
+    {
       const uint8_t* qrow =
           (const uint8_t*)(a.q + ((size_t)seq * Hq + (size_t)hg * HPU + hw * 16 + i16) * kDqk);
 #pragma unroll
@@ -325,129 +336,155 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_stream_kernel(MlaArgs a) {
       // (which do not know about the stage copies) would drain the copy pipeline at every
       // stage.
       wait_vm<0>();
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) o[ht][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      m_run = kNegInf;
-      l_part = 0.f;
     }
-    // stage n has landed once this wave's loads of it are done (NBUF - 2 newer stages may
-    // still be in flight) and every wave got here, which also means every wave is done
-    // reading the buffer that stage n + NBUF - 1 now overwrites
-    barrier_vm<kDmaPerWave * (NBUF - 2)>();
-    issue_stage(n + NBUF - 1);
-    const uint8_t* buf = sbuf + (n % NBUF) * kStageBytes;
+    // O is not cleared: with the running max back at -inf, the piece's first stage with a
+    // valid token rescales every head by alpha = 2^(-inf) = 0.  (A piece without valid
+    // tokens keeps m = -inf, and the merge gives it no weight.)
+    m_run = kNegInf;
+    l_part = 0.f;
+    for (; n < n_end; ++n) {
+      const int valid = stage_info(n) & 63;
+      // stage n has landed once this wave's loads of it are done (NBUF - 2 newer stages may
+      // still be in flight) and every wave got here, which also means every wave is done
+      // reading the buffer that stage n + NBUF - 1 now overwrites
+      barrier_vm<kDmaPerWave * (NBUF - 2)>();
+      issue_stage(n + NBUF - 1);
+      const uint8_t* buf = sbuf + (n % NBUF) * kStageBytes;
 
-    // ---- S^T = K Q^T for this wave's token tiles and head tile
-    f32x4_t s[TT];
+      // ---- S^T = K Q^T for this wave's token tiles and head tile; K fragments are read in
+      // groups of six ahead of their MFMAs
+      f32x4_t s[TT];
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) s[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int tt = 0; tt < TT; ++tt) s[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < kDqk / 32; ++ks) {
+      for (int k0 = 0; k0 < kDqk / 32; k0 += 6) {
+        bf16x8_t kf[TT][6];
+#pragma unroll
+        for (int ks = 0; ks < 6; ++ks)
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt)
+            kf[tt][ks] = __builtin_bit_cast(
+                bf16x8_t, *(const uint4*)(buf + k_off[tt][(k0 + ks) & 1] + 128 * ((k0 + ks) >> 1)));
+#pragma unroll
+        for (int ks = 0; ks < 6; ++ks)
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) s[tt] = mfma_bf16(kf[tt][ks], qf[k0 + ks], s[tt]);
+      }
+
+      // ---- online softmax (log2 domain); lane holds tokens tt*16 + 4g + r of head i16
+      float sv[TT * 4];
+      float mt = kNegInf;
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tok = (tt0 + tt) * 16 + 4 * g + r;
+          const float v = tok < valid ? s[tt][r] * cscale : kNegInf;
+          sv[tt * 4 + r] = v;
+          mt = fmaxf(mt, v);
+        }
+      mt = group_max4(mt);
+      if constexpr (WPH > 1) {  // the other token tile of this head tile is another wave's
+        if (g == 0) sMax[tt0 / TT][hw * 16 + i16] = mt;
+        barrier_vm<63>();
+        mt = fmaxf(sMax[0][hw * 16 + i16], sMax[1][hw * 16 + i16]);
+      }
+      float alpha = 1.f;
+      if (wave_any(mt > m_run + kSlack)) {
+        const float m_new = fmaxf(m_run, mt);
+        alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+        l_part *= alpha;
+        m_run = m_new;
+      }
+      if (tt0 == 0 && g == 0) sAlpha[hw * 16 + i16] = alpha;
+      const float m_use = (m_run == kNegInf) ? 0.f : m_run;
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
-        const bf16x8_t kf = __builtin_bit_cast(
-            bf16x8_t, *(const uint4*)(buf + k_off[tt][ks & 1] + 128 * (ks >> 1)));
-        s[tt] = mfma_bf16(kf, qf[ks], s[tt]);
+        const uint32_t p01 = pack_f16(fast_exp2(sv[tt * 4 + 0] - m_use), fast_exp2(sv[tt * 4 + 1] - m_use));
+        const uint32_t p23 = pack_f16(fast_exp2(sv[tt * 4 + 2] - m_use), fast_exp2(sv[tt * 4 + 3] - m_use));
+        l_part = dot2h(p01, kOnesF16x2, l_part);
+        l_part = dot2h(p23, kOnesF16x2, l_part);
+        *(uint2*)(sP + (hw * 16 + i16) * kPRow + ((tt0 + tt) * 16 + 4 * g) * 2) = uint2{p01, p23};
       }
-    }
-
-    // ---- online softmax (log2 domain); lane holds tokens tt*16 + 4g + r of head i16
-    float sv[TT * 4];
-    float mt = kNegInf;
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tok = (tt0 + tt) * 16 + 4 * g + r;
-        const float v = tok < valid ? s[tt][r] * cscale : kNegInf;
-        sv[tt * 4 + r] = v;
-        mt = fmaxf(mt, v);
-      }
-    mt = group_max4(mt);
-    if constexpr (WPH > 1) {  // the other token tile of this head tile is another wave's
-      if (g == 0) sMax[tt0 / TT][hw * 16 + i16] = mt;
       barrier_vm<63>();
-      mt = fmaxf(sMax[0][hw * 16 + i16], sMax[1][hw * 16 + i16]);
-    }
-    float alpha = 1.f;
-    if (wave_any(mt > m_run + kSlack)) {
-      const float m_new = fmaxf(m_run, mt);
-      alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
-      l_part *= alpha;
-      m_run = m_new;
-    }
-    if (tt0 == 0 && g == 0) sAlpha[hw * 16 + i16] = alpha;
-    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      const uint32_t p01 = pack_f16(fast_exp2(sv[tt * 4 + 0] - m_use), fast_exp2(sv[tt * 4 + 1] - m_use));
-      const uint32_t p23 = pack_f16(fast_exp2(sv[tt * 4 + 2] - m_use), fast_exp2(sv[tt * 4 + 3] - m_use));
-      l_part = dot2h(p01, kOnesF16x2, l_part);
-      l_part = dot2h(p23, kOnesF16x2, l_part);
-      *(uint2*)(sP + (hw * 16 + i16) * kPRow + ((tt0 + tt) * 16 + 4 * g) * 2) = uint2{p01, p23};
-    }
-    barrier_vm<63>();
 
-    // ---- O += P V for dims [128 w, 128 w + 128) of all HPU heads
-    {
-      float4 al[HT];
-      bool any = false;
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        al[ht] = *(const float4*)&sAlpha[ht * 16 + 4 * g];
-        any |= al[ht].x != 1.f || al[ht].y != 1.f || al[ht].z != 1.f || al[ht].w != 1.f;
-      }
-      if (wave_any(any)) {
+      // ---- O += P V for dims [128 w, 128 w + 128) of all HPU heads, after scaling O's rows
+      // by their heads' alpha when some head's running max moved (rare).  The accumulators
+      // live in ordinary VGPRs (this file is built with -amdgpu-mfma-vgpr-form): in the
+      // accumulator registers the compiler would copy them around this branch every stage.
+      auto pv_phase = [&]() {
+        // all P and V fragments are read first (V widened to fp16 as it arrives), then the
+        // HT x 8 MFMAs run back to back
+        f16x8_t pf[HT];
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht)
+          pf[ht] = __builtin_bit_cast(f16x8_t, *(const uint4*)(sP + (ht * 16 + i16) * kPRow + 16 * g));
+        const lds_char_t* lbuf = (const lds_char_t*)((lds_void_t*)buf);
+        uint2 vr[8][2];
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            vr[nt][h] = __builtin_bit_cast(
+                uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                           (lds_s16x4_t*)(lbuf + v_off[h][nt & 3] + 128 * (nt >> 2))));
+        sched_fence();
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          const f16x8_t vf = __builtin_bit_cast(
+              f16x8_t, uint4{bf16x2_to_f16x2(vr[nt][0].x), bf16x2_to_f16x2(vr[nt][0].y),
+                             bf16x2_to_f16x2(vr[nt][1].x), bf16x2_to_f16x2(vr[nt][1].y)});
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) o[ht][nt] = mfma_f16(pf[ht], vf, o[ht][nt]);
+        }
+      };
+      float4 alv[HT];
+      bool anyr = false;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        alv[ht] = *(const float4*)&sAlpha[ht * 16 + 4 * g];
+        anyr |= alv[ht].x != 1.f || alv[ht].y != 1.f || alv[ht].z != 1.f || alv[ht].w != 1.f;
+      }
+      if (wave_any(anyr)) {
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+          const float4 al = alv[ht];
 #pragma unroll
           for (int nt = 0; nt < 8; ++nt) {
-            o[ht][nt][0] *= al[ht].x;
-            o[ht][nt][1] *= al[ht].y;
-            o[ht][nt][2] *= al[ht].z;
-            o[ht][nt][3] *= al[ht].w;
+            o[ht][nt][0] *= al.x;
+            o[ht][nt][1] *= al.y;
+            o[ht][nt][2] *= al.z;
+            o[ht][nt][3] *= al.w;
           }
+        }
       }
+      pv_phase();
     }
-    f16x8_t pf[HT];
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
-      pf[ht] = __builtin_bit_cast(f16x8_t, *(const uint4*)(sP + (ht * 16 + i16) * kPRow + 16 * g));
-    const lds_char_t* lbuf = (const lds_char_t*)((lds_void_t*)buf);
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      uint32_t vw[4];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)(lbuf + v_off[h][nt & 3] + 128 * (nt >> 2)));
-        const uint2 rr = __builtin_bit_cast(uint2, r);
-        vw[2 * h] = bf16x2_to_f16x2(rr.x);
-        vw[2 * h + 1] = bf16x2_to_f16x2(rr.y);
-      }
-      const f16x8_t vf = __builtin_bit_cast(f16x8_t, uint4{vw[0], vw[1], vw[2], vw[3]});
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) o[ht][nt] = mfma_f16(pf[ht], vf, o[ht][nt]);
-    }
+    flush();
   }
-  flush();
   // Copies of stages past the end (empty ranges) may still be in flight: they must land
   // before this workgroup's LDS can be handed to another one.
   wait_vm<0>();
 }
 
-int mla_stream_heads_per_group(int Hq) { return (Hq % 32 == 0 && Hq <= 128) ? 32 : 0; }
+// 64 heads per workgroup (two waves' worth of p.V accumulators per wave) where Hq allows,
+// else 32.
+int mla_stream_heads_per_group(int Hq) {
+  if (Hq > 128) return 0;
+  return Hq % 64 == 0 ? 64 : (Hq % 32 == 0 ? 32 : 0);
+}
 
 hipError_t launch_mla_stream(const MlaArgs& a, hipStream_t s) {
-  constexpr int HT = 2, NBUF = 4;
-  if (a.d_qk != kDqk || a.d_v != kDv || a.block_size != kBlock || a.B > kMaxMlaSeqs ||
-      mla_stream_heads_per_group(a.Hq) != 16 * HT || a.chunks % 8)
+  constexpr int NBUF = 4;
+  const int hpu = mla_stream_heads_per_group(a.Hq);
+  if (a.d_qk != kDqk || a.d_v != kDv || a.block_size != kBlock || a.B > kMaxMlaSeqs || !hpu ||
+      a.chunks % 8)
     return hipErrorInvalidValue;
-  const int HG = a.Hq / (16 * HT);
-  hipLaunchKernelGGL((mla_stream_kernel<HT, NBUF>), dim3((unsigned)(HG * a.chunks)),
-                     dim3(kMThreads), 0, s, a);
+  const dim3 grid((unsigned)(a.Hq / hpu * a.chunks));
+  if (hpu == 64)
+    hipLaunchKernelGGL((mla_stream_kernel<4, NBUF>), grid, dim3(kMThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((mla_stream_kernel<2, NBUF>), grid, dim3(kMThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   DecodeArgs m{};

@@ -194,7 +194,7 @@ def test_binding_refuses_to_run_without_library(monkeypatch, tmp_path):
 
 
 def _mla_chunks(B, Hq, ctx, cus):
-    hg = Hq // 32
+    hg = Hq // (64 if Hq % 64 == 0 else 32)   # head groups of 64 (or 32) heads
     c = max(-(-cus // hg), -(-(B * -(-ctx // 32)) // 128))
     return -(-c // 8) * 8
 
