@@ -31,12 +31,13 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attn: KV GB/s read & % of MI355X HBM peak; decode tokens/s"
 HBM_PEAK_GBS = 8000.0                       # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0              # MI355X dense bf16 / fp16 matrix peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "gqa": ["paged_kv_cache_288_amd/csrc/gqa_stream.hip", "paged_kv_cache_288_amd/csrc/gqa_decode.hip",
             "paged_kv_cache_288_amd/csrc/gqa_tile.hpp", "paged_kv_cache_288_amd/csrc/pkv_device.hpp"],
-    "mla": ["paged_kv_cache_288_amd/csrc/mla_decode.hip", "paged_kv_cache_288_amd/csrc/gqa_decode.hip",
-            "paged_kv_cache_288_amd/csrc/pkv_device.hpp"],
+    "mla": ["paged_kv_cache_288_amd/csrc/mla_stream.hip", "paged_kv_cache_288_amd/csrc/gqa_stream.hip",
+            "paged_kv_cache_288_amd/csrc/gqa_tile.hpp", "paged_kv_cache_288_amd/csrc/pkv_device.hpp"],
 }
 
 
@@ -78,7 +79,9 @@ def traffic_for(workload_name, kind):
 
 def kernel_label(w, pkv, ps):
     if w.kind == "mla":
-        return "pkv_paged_decode_attn_mla call (mla_decode_kernel + partition_merge_kernel<512>)"
+        if ps == 0 and w.Hq % 32 == 0 and w.Hq <= 128:
+            return "pkv_paged_decode_attn_mla call, balanced mode (mla_stream_kernel + stream_merge_kernel<512>)"
+        return "pkv_paged_decode_attn_mla call, partitioned (mla_decode_kernel + partition_merge_kernel<512>)"
     if pkv.decode_partition_size(w.B, w.Hkv, w.max_context_len, ps) == 0:
         return "pkv_paged_decode_attn call, balanced mode (gqa_stream_kernel + stream_merge_kernel)"
     return "pkv_paged_decode_attn call, partitioned (gqa_decode_kernel + partition_merge_kernel)"
@@ -233,6 +236,28 @@ def main():
     kvb = kv_bytes(w)
     call_avg = float(call_ms.mean())
     achieved = kvb / (call_avg * 1e-3) / 1e9
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(achieved, 2),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+    }
+    if w.kind == "mla":
+        # the latent case is a dense contraction on the matrix cores: scores (d_qk) and
+        # p.V (d_v) for every query head and cached token
+        flops = float(w.context_lens.astype(np.int64).sum()) * w.Hq * 2 * (w.d + w.d_v)
+        tflops = flops / (call_avg * 1e-3) / 1e12
+        roofline = {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "algorithmic_flops_per_call": flops,
+            "hbm_achieved_GBs": round(achieved, 2),
+            "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
+        }
     result = {
         "metric": METRIC,
         "value": round(kvb / (ms_per_step * 1e-3) / 1e9, 2),
@@ -259,11 +284,7 @@ def main():
         "decode_tokens_per_s": round(w.B / (ms_per_step * 1e-3), 1),
         "hbm_peak_frac_step": round(kvb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            **roofline,
             "traffic": traffic_for(w.name, w.kind),
             "kernel": kernel_label(w, pkv, ps),
             "call_ms_avg": round(call_avg, 5),
