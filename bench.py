@@ -21,6 +21,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -45,11 +46,19 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def _code_only(text):
+    """Source text without comments and blank lines: what the compiler sees of it."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def kernel_hash(kind):
+    """Hash of the kernel sources' code (comments ignored), keying stored counter data."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

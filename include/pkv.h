@@ -144,6 +144,8 @@ size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d_
  * Precision: scores accumulate exact bf16 (or widened FP8) products in fp32; the
  * softmax weights are rounded to fp16 and V widened to fp16 for p.V, accumulated in fp32.
  * bf16 V values must therefore lie within fp16's range (|v| < 65504); FP8 values always do.
+ * (bf16 values below 2^-14 in magnitude land on fp16's subnormal grid: absolute error
+ * at most 2^-25 per value.)
  */
 pkv_status pkv_paged_decode_attn(float* out, const void* q, const void* k_pool,
                                  const void* v_pool, const float* k_scale, const float* v_scale,
@@ -177,7 +179,8 @@ size_t pkv_mla_workspace_bytes(int32_t B, int32_t Hq, int32_t d_v, int32_t max_c
  *   (partition_size a multiple of block_size, or 0 for the library's choice).
  * Supported: d_qk = 576, d_v = 512, block_size = 64, Hq a multiple of 16 (<= 128).
  * Precision: scores on the bf16 MFMA (fp32 accumulate); weights and the value dims in fp16
- * on the fp16 MFMA for p.V, so latent values must satisfy |v| < 65504.
+ * on the fp16 MFMA for p.V, so latent values must satisfy |v| < 65504 (values below 2^-14
+ * in magnitude are rounded to fp16's subnormal grid, absolute error at most 2^-25).
  */
 pkv_status pkv_paged_decode_attn_mla(float* out, const void* q, const void* kv_pool,
                                      const int32_t* block_table, const int32_t* context_lens,

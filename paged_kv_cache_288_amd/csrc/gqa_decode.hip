@@ -22,10 +22,14 @@
 //           8*dc..8*dc+7; its accumulators o[h][8] cover those tokens only (4 independent
 //           row states, merged once at the end).  The tokens a row needs for p.V are the
 //           ones its own lanes scored, so probabilities move by DPP row broadcasts.
-//  * Both products use v_dot2c_f32_bf16: q.K pairs adjacent dims, p.V pairs two tokens
-//           (probabilities rounded to bf16, V rows interleaved with v_perm_b32).  FP8 E4M3
-//           K/V are widened to bf16 pairs with v_cvt_scalef32_pk_bf16_fp8 (exact); the
-//           per-head K scale folds into the score scale and the V scale into the output.
+//  * q.K runs on v_dot2_f32_bf16 over adjacent dims; p.V on v_dot2_f32_f16 over two tokens
+//           (probabilities rounded to fp16, V rows widened bf16 -> fp16 and paired token by
+//           token in registers).  FP8 E4M3 K is widened to bf16 pairs and V to fp16 pairs
+//           (both exact); the per-head K scale folds into the score scale and the V scale
+//           into the output.
+//  * K/V are read through range-checked buffer resources whose range ends at the tile's
+//           last valid token, so rows past a sequence's end are read as zeros (and carry
+//           zero probability), whatever the pool holds there.
 // Online softmax runs in the log2 domain with a lazy rescale: the running max only moves
 // (rescaling o and l) when a new score exceeds it by more than 2^8, which keeps every
 // probability <= 256 and skips almost all rescales after the first tile.

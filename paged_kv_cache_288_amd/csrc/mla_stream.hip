@@ -33,7 +33,8 @@
 //  * p.V: O += P V on v_mfma_f32_16x16x32_f16.  A wave owns 128 of the 512 output dims for
 //    all heads of the group.  The B operand (8 tokens of one dim per lane) is read from the
 //    token-major rows with ds_read_b64_tr_b16, which transposes 4x4 blocks of 16-bit values
-//    across lanes, and widened bf16 -> fp16 in registers (exact for |v| < 65504).
+//    across lanes, and widened bf16 -> fp16 in registers (exact in fp16's normal range,
+//    below 2^-14 rounded to its subnormal grid; |v| must stay below 65504).
 #include "pkv_device.hpp"
 #include "pkv_launch.hpp"
 
