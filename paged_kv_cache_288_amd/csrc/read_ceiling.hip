@@ -1,5 +1,8 @@
 // Achievable HBM read bandwidth on this GPU: a grid-stride kernel reading a 4 GiB buffer
-// with 16-byte loads (plain and nontemporal), for comparison with the decode kernels.
+// with 16-byte loads (plain and nontemporal), and scattered whole-chunk reads as a paged KV
+// cache does, for comparison with the decode kernels.  Every configuration runs twice: on a
+// buffer of one repeated byte and on pseudo-random bits (KV data is random; the two agree to
+// about 1 %, so the ceiling does not depend on the data).
 // Usage: read_ceiling   (prints one line per configuration, GB/s)
 #include <hip/hip_runtime.h>
 
@@ -43,6 +46,18 @@ __global__ void chunk_kernel(const u32x4* __restrict__ p, size_t nchunks, uint32
     for (int u = 0; u < PER; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
   if (acc == 0x12345678u) out[blockIdx.x] = acc;
+}
+
+// Pseudo-random 32-bit words (an integer hash of the index; any well-mixed bits will do).
+__global__ void fill_random(uint32_t* p, size_t n, uint32_t seed) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    uint32_t x = (uint32_t)i * 2654435761u ^ seed;
+    x ^= x >> 13;
+    x *= 0x5bd1e995u;
+    x ^= x >> 15;
+    p[i] = x;
+  }
 }
 
 template <int CHUNK, bool NT>
@@ -96,18 +111,26 @@ int main() {
     printf("allocation failed\n");
     return 1;
   }
-  (void)hipMemset(p, 1, bytes);
-  (void)hipDeviceSynchronize();
-  for (int blocks : {1024, 2048, 4096, 8192}) {
-    run<4, false>(p, n16, out, blocks);
-    run<8, false>(p, n16, out, blocks);
-    run<4, true>(p, n16, out, blocks);
-  }
-  for (int blocks : {2048, 8192}) {
-    run_chunks<4096, false>(p, bytes, out, blocks);
-    run_chunks<4096, true>(p, bytes, out, blocks);
-    run_chunks<8192, true>(p, bytes, out, blocks);
-    run_chunks<16384, true>(p, bytes, out, blocks);
+  for (int pass = 0; pass < 2; ++pass) {
+    if (pass == 0) {
+      (void)hipMemset(p, 1, bytes);
+      printf("-- data: every byte 0x01\n");
+    } else {
+      hipLaunchKernelGGL(fill_random, dim3(4096), dim3(256), 0, 0, (uint32_t*)p, bytes / 4, 12345u);
+      printf("-- data: pseudo-random bits\n");
+    }
+    (void)hipDeviceSynchronize();
+    for (int blocks : {1024, 2048, 4096, 8192}) {
+      run<4, false>(p, n16, out, blocks);
+      run<8, false>(p, n16, out, blocks);
+      run<4, true>(p, n16, out, blocks);
+    }
+    for (int blocks : {2048, 8192}) {
+      run_chunks<4096, false>(p, bytes, out, blocks);
+      run_chunks<4096, true>(p, bytes, out, blocks);
+      run_chunks<8192, true>(p, bytes, out, blocks);
+      run_chunks<16384, true>(p, bytes, out, blocks);
+    }
   }
   (void)hipFree(p);
   (void)hipFree(out);
