@@ -107,7 +107,7 @@ int32_t pkv_decode_partition_size(int32_t B, int32_t Hkv, int32_t max_context_le
  * arguments on the current device (0 when a partitioned context is not split).  The
  * workspace holds the partial online-softmax states (running max, sum and unnormalised
  * output per query head) of partitions, or of the balanced mode's pieces, plus (balanced
- * mode) the per-sequence tile prefix the merge step reads.
+ * mode) the per-sequence tile prefix and per-segment piece ranges the merge step reads.
  */
 size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d_v,
                                   int32_t max_context_len, int32_t partition_size);

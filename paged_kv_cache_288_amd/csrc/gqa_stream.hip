@@ -23,11 +23,6 @@ namespace pkv {
 constexpr int kMaxStreamSeqs = 4096;  // sequences whose tile counts fit the LDS prefix
 constexpr int kMaxChunkTiles = 128;   // tiles per chunk: two per lane
 
-// First chunk whose range holds flattened tile t (chunk c covers [T*c/C, T*(c+1)/C)).
-__device__ __forceinline__ int chunk_of(long long t, long long T, int C) {
-  return (int)(((t + 1) * (long long)C - 1) / T);
-}
-
 template <int D, int G, bool FP8>
 __global__ __launch_bounds__(kWaves * kWave, 2) void gqa_stream_kernel(DecodeArgs a) {
   using Lo = Layout<D, FP8>;
@@ -69,8 +64,10 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void gqa_stream_kernel(DecodeArg
   }
   if (tid == 0) s_pre[B] = s_sum[kWaves * kWave - 1];
   __syncthreads();
-  if (blockIdx.x == 0)
+  if (blockIdx.x == 0) {
     for (int i = tid; i <= B; i += kWaves * kWave) a.ws_prefix[i] = s_pre[i];
+    write_segment_ranges(a.ws_seg, s_pre, B, a.Hkv, a.chunks, tid, kWaves * kWave);
+  }
 
   // ---- this wave's chunk
   const int T_head = __builtin_amdgcn_readfirstlane(s_pre[B]);
@@ -232,29 +229,31 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void gqa_stream_kernel(DecodeArg
 }
 
 // out[b][h] = sum over the pieces of segment (g = h / G, b) of 2^(m - M) o / 2^(m - M) l.
-// One wave per (sequence, query head).
+// One wave per (sequence, query head), kMergeWaves of them per workgroup.
+constexpr int kMergeWaves = 4;
 template <int D>
-__global__ __launch_bounds__(kWave) void stream_merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kMergeWaves * kWave) void stream_merge_kernel(DecodeArgs a) {
   constexpr int PER = D / kWave;
   const int G = a.Hq / a.Hkv;
-  const int bh = blockIdx.x, b = bh / a.Hq, hq = bh - b * a.Hq, g = hq / G, h = hq - g * G;
-  const int lane = threadIdx.x;
+  const int bh = blockIdx.x * kMergeWaves + (int)(threadIdx.x / kWave);
+  if (bh >= a.B * a.Hq) return;
+  const int b = bh / a.Hq, hq = bh - b * a.Hq, g = hq / G, h = hq - g * G;
+  const int lane = threadIdx.x & (kWave - 1);
   float* out = a.out + (size_t)bh * D;
+  const int c0 = a.ws_seg[2 * (g * a.B + b)], np = a.ws_seg[2 * (g * a.B + b) + 1];
   const int T_head = a.ws_prefix[a.B];
-  const int nb = a.ws_prefix[b + 1] - a.ws_prefix[b];
-  if (nb == 0) {
+  if (np == 0) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) out[lane + kWave * i] = 0.f;
     return;
   }
   const long long T = (long long)a.Hkv * T_head;
-  const long long s0 = (long long)g * T_head + a.ws_prefix[b];
-  const int c0 = chunk_of(s0, T, a.chunks), c1 = chunk_of(s0 + nb - 1, T, a.chunks);
-  const int np = c1 - c0 + 1;
   const size_t slot0 = (size_t)c0 + (size_t)g * a.B + b;  // slot of piece i: slot0 + i
-  // Chunks c0..c1 cover the segment, but when there are fewer tiles than chunks some of
-  // them are empty and wrote nothing: those carry no weight and are never read.
+  // Chunks c0 .. c0 + np - 1 cover the segment.  With fewer tiles than chunks some of them
+  // are empty and wrote nothing: those carry no weight and are never read.
+  const bool all_live = T >= a.chunks;
   auto live = [&](int i) {
+    if (all_live) return true;
     const long long cc = c0 + i;
     return T * cc / a.chunks != T * (cc + 1) / a.chunks;
   };
@@ -306,10 +305,10 @@ static hipError_t launch_stream_d(const DecodeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_stream_merge(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)a.B * a.Hq);
-  if (a.d == 128) hipLaunchKernelGGL(stream_merge_kernel<128>, grid, dim3(kWave), 0, s, a);
-  else if (a.d == 64) hipLaunchKernelGGL(stream_merge_kernel<64>, grid, dim3(kWave), 0, s, a);
-  else if (a.d == 512) hipLaunchKernelGGL(stream_merge_kernel<512>, grid, dim3(kWave), 0, s, a);
+  const dim3 grid((unsigned)((a.B * a.Hq + kMergeWaves - 1) / kMergeWaves)), block(kMergeWaves * kWave);
+  if (a.d == 128) hipLaunchKernelGGL(stream_merge_kernel<128>, grid, block, 0, s, a);
+  else if (a.d == 64) hipLaunchKernelGGL(stream_merge_kernel<64>, grid, block, 0, s, a);
+  else if (a.d == 512) hipLaunchKernelGGL(stream_merge_kernel<512>, grid, block, 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

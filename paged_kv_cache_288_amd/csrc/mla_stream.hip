@@ -173,8 +173,10 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_stream_kernel(MlaArgs a) {
     }
     if (tid == 0) s_pre[B] = s_sum[kMThreads - 1];
     __syncthreads();
-    if (blockIdx.x == 0)
+    if (blockIdx.x == 0) {
       for (int i = tid; i <= B; i += kMThreads) a.ws_prefix[i] = s_pre[i];
+      write_segment_ranges(a.ws_seg, s_pre, B, 1, C, tid, kMThreads);
+    }
   }
 
   // ---- this workgroup's head group and chunk: the HG head groups of chunk ch are
@@ -499,6 +501,7 @@ hipError_t launch_mla_stream(const MlaArgs& a, hipStream_t s) {
   m.d = kDv;
   m.chunks = a.chunks;
   m.ws_prefix = a.ws_prefix;
+  m.ws_seg = a.ws_seg;
   return launch_stream_merge(m, s);
 }
 

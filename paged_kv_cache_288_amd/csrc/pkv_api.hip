@@ -92,12 +92,14 @@ int32_t stream_chunks(int32_t B, int32_t Hkv, int32_t max_ctx) {
   return c > (1LL << 30) ? -1 : (int32_t)c;
 }
 
-// Balanced-mode workspace: m [S][G], l [S][G], o [S][G][d], prefix [B + 1] (int32),
-// S = chunks + Hkv * B piece slots; sections 256-byte aligned.
+// Balanced-mode workspace: m [S][G], l [S][G], o [S][G][d], prefix [B + 1] (int32) and
+// per-segment (first chunk, chunks spanned) [Hkv * B][2] (int32), S = chunks + Hkv * B piece
+// slots; sections 256-byte aligned.
 size_t stream_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t chunks) {
   const size_t rows = ((size_t)chunks + (size_t)Hkv * B) * (size_t)(Hq / Hkv);
   return 2 * round256(rows * sizeof(float)) + round256(rows * d * sizeof(float)) +
-         round256(((size_t)B + 1) * sizeof(int32_t));
+         round256(((size_t)B + 1) * sizeof(int32_t)) +
+         round256((size_t)Hkv * B * 2 * sizeof(int32_t));
 }
 
 // Latent balanced mode: one 4-wave workgroup per CU, Hq / 32 head groups, chunks a
@@ -231,10 +233,11 @@ pkv_status pkv_paged_decode_attn(float* out, const void* q, const void* k_pool,
     float* ws_o = (float*)(base + 2 * round256(rows * sizeof(float)));
     int32_t* ws_p = (int32_t*)(base + 2 * round256(rows * sizeof(float)) +
                                round256(rows * d * sizeof(float)));
+    int32_t* ws_s = (int32_t*)((char*)ws_p + round256(((size_t)B + 1) * sizeof(int32_t)));
     pkv::DecodeArgs a{out, (const uint16_t*)q, (const uint8_t*)k_pool, (const uint8_t*)v_pool,
                       k_scale, v_scale, block_table, context_lens, ws_m, ws_l, ws_o,
                       B, Hq, Hkv, d, block_size, num_blocks, max_blocks_per_seq, ctx,
-                      0, 0, scale, fp8 ? 1 : 0, chunks, ws_p};
+                      0, 0, scale, fp8 ? 1 : 0, chunks, ws_p, ws_s};
     return hip_status(pkv::launch_gqa_stream(a, s));
   }
   const int32_t P = num_parts(ctx, ps);
@@ -302,9 +305,10 @@ pkv_status pkv_paged_decode_attn_mla(float* out, const void* q, const void* kv_p
     float* ws_o = (float*)(base + 2 * round256(rows * sizeof(float)));
     int32_t* ws_p = (int32_t*)(base + 2 * round256(rows * sizeof(float)) +
                                round256(rows * d_v * sizeof(float)));
+    int32_t* ws_s = (int32_t*)((char*)ws_p + round256(((size_t)B + 1) * sizeof(int32_t)));
     pkv::MlaArgs a{out, (const uint16_t*)q, (const uint16_t*)kv_pool, block_table, context_lens,
                    ws_m, ws_l, ws_o, B, Hq, d_qk, d_v, block_size, num_blocks,
-                   max_blocks_per_seq, ctx, 0, 0, scale, chunks, ws_p};
+                   max_blocks_per_seq, ctx, 0, 0, scale, chunks, ws_p, ws_s};
     return hip_status(pkv::launch_mla_stream(a, s));
   }
   const int32_t ps = partition_size > 0 ? partition_size : mla_auto_partition(B, Hq, ctx);

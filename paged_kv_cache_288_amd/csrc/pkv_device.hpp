@@ -140,4 +140,32 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
+// ---------------------------------------------------------------- balanced-mode bookkeeping
+// The balanced kernels lay the units of work (16-token tiles, or stages) of all (head g,
+// sequence b) segments end to end, head-major, and cut the T units into C equal ranges:
+// range c covers [T c / C, T (c + 1) / C).  First range holding unit t:
+__device__ __forceinline__ int chunk_of(long long t, long long T, int C) {
+  return (int)(((t + 1) * (long long)C - 1) / T);
+}
+// For the merge kernel, per segment s = g * B + b: the first range holding its units and the
+// number of ranges it spans (0 for a sequence without units).  pre[0..B] is the exclusive
+// prefix of units per sequence; threads tid, tid + nthreads, ... of one workgroup write.
+__device__ __forceinline__ void write_segment_ranges(int32_t* ws_seg, const int* pre, int B,
+                                                     int H, int C, int tid, int nthreads) {
+  const int T_head = pre[B];
+  const long long T = (long long)H * T_head;
+  for (int sg = tid; sg < H * B; sg += nthreads) {
+    const int g = sg / B, b = sg - g * B;
+    const int nb = pre[b + 1] - pre[b];
+    int c0 = 0, n = 0;
+    if (nb > 0) {
+      const long long first = (long long)g * T_head + pre[b];
+      c0 = chunk_of(first, T, C);
+      n = chunk_of(first + nb - 1, T, C) - c0 + 1;
+    }
+    ws_seg[2 * sg] = c0;
+    ws_seg[2 * sg + 1] = n;
+  }
+}
+
 }  // namespace pkv

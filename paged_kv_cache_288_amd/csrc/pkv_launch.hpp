@@ -35,10 +35,12 @@ struct DecodeArgs {
   int32_t partition, num_partitions;  // num_partitions == 1: no split, out written directly
   float scale;
   int32_t fp8;
-  // balanced mode: number of equal chunks (one per wave, a multiple of 32) and the
-  // per-sequence tile prefix [B + 1] the decode kernel leaves for the merge kernel
+  // balanced mode: number of equal chunks (one per wave, a multiple of 32), and what the
+  // decode kernel leaves for the merge kernel: the per-sequence tile prefix [B + 1] and per
+  // segment (first chunk, chunks spanned) [Hkv * B][2]
   int32_t chunks;
   int32_t* ws_prefix;
+  int32_t* ws_seg;
 };
 hipError_t launch_gqa_decode(const DecodeArgs& a, hipStream_t s);
 // Balanced mode: decode kernel + merge kernel (always both).
@@ -63,10 +65,12 @@ struct MlaArgs {
   int32_t B, Hq, d_qk, d_v, block_size, num_blocks, max_blocks, max_context_len;
   int32_t partition, num_partitions;
   float scale;
-  // balanced mode: chunks per head group (a multiple of 8) and the per-sequence stage prefix
-  // [B + 1] the decode kernel leaves for the merge kernel
+  // balanced mode: chunks per head group (a multiple of 8), and what the decode kernel leaves
+  // for the merge kernel: the per-sequence stage prefix [B + 1] and per sequence (first
+  // chunk, chunks spanned) [B][2]
   int32_t chunks;
   int32_t* ws_prefix;
+  int32_t* ws_seg;
 };
 hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t s);
 // Balanced mode: decode kernel + merge kernel.  Heads per workgroup for a given Hq

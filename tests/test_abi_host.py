@@ -126,7 +126,7 @@ def test_balanced_mode_workspace_size(lib):
     for B, Hq, Hkv, d, ctx in [(64, 64, 8, 128, 8192), (2, 4, 1, 64, 256), (4, 64, 8, 128, 32768)]:
         C = _stream_chunks(B, Hkv, ctx, 256)
         rows = (C + Hkv * B) * (Hq // Hkv)
-        want = 2 * r256(rows * 4) + r256(rows * d * 4) + r256((B + 1) * 4)
+        want = 2 * r256(rows * 4) + r256(rows * d * 4) + r256((B + 1) * 4) + r256(Hkv * B * 8)
         assert lib.pkv_decode_workspace_bytes(B, Hq, Hkv, d, ctx, 0) == want
 
 
@@ -201,14 +201,15 @@ def _mla_chunks(B, Hq, ctx, cus):
 
 def test_mla_balanced_workspace_size(lib):
     """Latent balanced mode (partition_size 0, Hq a multiple of 32): pieces (chunks + B) x Hq
-    rows of m, l and o[512], plus the stage prefix; 256 CUs assumed without a GPU."""
+    rows of m, l and o[512], the stage prefix and per-sequence chunk ranges; 256 CUs assumed
+    without a GPU."""
     r256 = lambda x: (x + 255) // 256 * 256
     for B, Hq, ctx in [(32, 128, 8192), (1, 32, 8192), (200, 64, 100), (5, 96, 1500),
                        (4, 128, 131072)]:
         C = _mla_chunks(B, Hq, ctx, 256)
         assert B * -(-ctx // 32) <= 128 * C            # no range exceeds 128 stages
         rows = (C + B) * Hq
-        want = 2 * r256(rows * 4) + r256(rows * 512 * 4) + r256((B + 1) * 4)
+        want = 2 * r256(rows * 4) + r256(rows * 512 * 4) + r256((B + 1) * 4) + r256(B * 8)
         assert lib.pkv_mla_workspace_bytes(B, Hq, 512, ctx, 0) == want
     # Hq not a multiple of 32 (and explicit partitions) use the partitioned kernel
     assert lib.pkv_mla_workspace_bytes(2, 48, 512, 8192, 0) > 0
