@@ -57,14 +57,13 @@ constexpr int kStage = 32;                          // tokens per stage
 constexpr int kRow = kDqk * 2;                      // 1152 bytes per latent row
 constexpr int kRowChunks = kRow / 16;               // 72
 constexpr int kStageBytes = kStage * kRow;          // 36864
-constexpr int kMWaves = 4;
-constexpr int kMThreads = kMWaves * kWave;
-constexpr int kDmaPerWave = kStageBytes / (16 * kWave) / kMWaves;  // 9 loads per wave per stage
+constexpr int kDmaWaves = 4;                        // waves that copy the stages
+constexpr int kDmaPerWave = kStageBytes / (16 * kWave) / kDmaWaves;  // 9 loads per wave per stage
 constexpr int kMaxMlaSeqs = 4096;
 constexpr int kMaxChunkStages = 128;                // two per lane
 constexpr int kPRow = 80;                           // bytes per head row of P (32 fp16 + pad)
 constexpr float kSlack = 8.0f;
-static_assert(kStageBytes % (16 * kWave * kMWaves) == 0, "stage split");
+static_assert(kStageBytes % (16 * kWave * kDmaWaves) == 0, "stage split");
 
 __device__ __forceinline__ f32x4_t mfma_bf16(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -123,18 +122,21 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t x) {
 
 }  // namespace
 
-template <int HT, int NBUF>
-__global__ __launch_bounds__(kMThreads, 1) void mla_stream_kernel(MlaArgs a) {
+template <int HT, int NW, int NBUF>
+__global__ __launch_bounds__(NW * kWave, 1) void mla_stream_kernel(MlaArgs a) {
+  constexpr int THREADS = NW * kWave;
   constexpr int HPU = 16 * HT;   // heads per workgroup
-  constexpr int WPH = 4 / HT;    // waves per head tile in the score phase
+  constexpr int WPH = NW / HT;   // waves per head tile in the score phase
   constexpr int TT = 2 / WPH;    // token tiles per wave in the score phase
-  static_assert(HT == 2 || HT == 4, "head tiles per workgroup");
+  constexpr int DPW = kDv / NW;  // output dims per wave in the p.V phase
+  constexpr int NT = DPW / 16;   // p.V products per head tile
+  static_assert((HT == 2 && NW == 4) || (HT == 4 && (NW == 4 || NW == 8)), "wave layout");
   __shared__ __attribute__((aligned(16))) uint8_t sbuf[NBUF * kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t sP[HPU * kPRow];
   __shared__ __attribute__((aligned(16))) float sMax[2][HPU];
   __shared__ __attribute__((aligned(16))) float sAlpha[HPU];
-  __shared__ float sL[kMWaves][16];
-  static_assert((kMaxMlaSeqs + 1 + kMThreads) * 4 <= NBUF * kStageBytes, "prefix scratch");
+  __shared__ float sL[NW][16];
+  static_assert((kMaxMlaSeqs + 1 + THREADS) * 4 <= NBUF * kStageBytes, "prefix scratch");
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
@@ -151,13 +153,13 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_stream_kernel(MlaArgs a) {
     return (L + kStage - 1) / kStage;
   };
   {
-    const int per = (B + kMThreads - 1) / kMThreads;
+    const int per = (B + THREADS - 1) / THREADS;
     int local = 0;
     for (int i = 0; i < per; ++i)
       if (tid * per + i < B) local += nstages(tid * per + i);
     s_sum[tid] = local;
     __syncthreads();
-    for (int off = 1; off < kMThreads; off <<= 1) {
+    for (int off = 1; off < THREADS; off <<= 1) {
       const int v = tid >= off ? s_sum[tid - off] : 0;
       __syncthreads();
       s_sum[tid] += v;
@@ -171,11 +173,11 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_stream_kernel(MlaArgs a) {
         run += nstages(bi);
       }
     }
-    if (tid == 0) s_pre[B] = s_sum[kMThreads - 1];
+    if (tid == 0) s_pre[B] = s_sum[THREADS - 1];
     __syncthreads();
     if (blockIdx.x == 0) {
-      for (int i = tid; i <= B; i += kMThreads) a.ws_prefix[i] = s_pre[i];
-      write_segment_ranges(a.ws_seg, s_pre, B, 1, C, tid, kMThreads);
+      for (int i = tid; i <= B; i += THREADS) a.ws_prefix[i] = s_pre[i];
+      write_segment_ranges(a.ws_seg, s_pre, B, 1, C, tid, THREADS);
     }
   }
 
@@ -234,14 +236,14 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_stream_kernel(MlaArgs a) {
   // The prefix scratch is dead from here on; clear the stage buffers once so that rows a
   // stage does not load hold zeros or earlier valid rows, never garbage.
   __syncthreads();
-  for (int i = tid; i < NBUF * kStageBytes / 16; i += kMThreads)
+  for (int i = tid; i < NBUF * kStageBytes / 16; i += THREADS)
     *(uint4*)(sbuf + 16 * i) = uint4{0, 0, 0, 0};
   __syncthreads();
   if (ns <= 0) return;
 
-  // ---- LDS-direct copy of a stage: load j of wave w fills bytes [1024 (9w + j), +1024) of
-  // the buffer; lane -> chunk c = 64 (9w + j) + lane = row t, permuted chunk p'; it loads
-  // chunk p' ^ swizzle(t) of row t from the pool.
+  // ---- LDS-direct copy of a stage by waves 0-3: load j of wave w fills bytes
+  // [1024 (9w + j), +1024) of the buffer; lane -> chunk c = 64 (9w + j) + lane = row t,
+  // permuted chunk p'; it loads chunk p' ^ swizzle(t) of row t from the pool.
   uint32_t dma_off[kDmaPerWave];
 #pragma unroll
   for (int j = 0; j < kDmaPerWave; ++j) {
@@ -251,6 +253,7 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_stream_kernel(MlaArgs a) {
   }
   const uint32_t sbuf_lds = (uint32_t)(uintptr_t)(lds_void_t*)sbuf;
   auto issue_stage = [&](int n) {
+    if (w >= kDmaWaves) return;
     const i32x4_t src = stage_src(n);
     const uint32_t base = sbuf_lds + (n % NBUF) * kStageBytes + w * kDmaPerWave * 1024;
 #pragma unroll
@@ -278,16 +281,16 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_stream_kernel(MlaArgs a) {
     const int qd = (i16 & 3) >> 1, half8 = 8 * (i16 & 1);
 #pragma unroll
     for (int n4 = 0; n4 < 4; ++n4)
-      v_off[h][n4] = 16 * (t * kRowChunks + 16 * w + ((2 * n4 + qd) ^ row_swizzle(t))) + half8;
+      v_off[h][n4] = 16 * (t * kRowChunks + (DPW / 8) * w + ((2 * n4 + qd) ^ row_swizzle(t))) + half8;
   }
 
   // ---- state
   bf16x8_t qf[kDqk / 32];
-  f32x4_t o[HT][8];
+  f32x4_t o[HT][NT];
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) o[ht][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};  // finite for alpha = 0
+    for (int nt = 0; nt < NT; ++nt) o[ht][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};  // finite for alpha = 0
   float m_run = kNegInf, l_part = 0.f;
   const float cscale = a.scale * kLog2e;
   int seq = -1;
@@ -308,10 +311,10 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_stream_kernel(MlaArgs a) {
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          a.ws_o[(row0 + ht * 16 + 4 * g + r) * kDv + 128 * w + 16 * nt + i16] = o[ht][nt][r];
+          a.ws_o[(row0 + ht * 16 + 4 * g + r) * kDv + DPW * w + 16 * nt + i16] = o[ht][nt][r];
   };
 
   for (int n = 0; n < NBUF - 1; ++n) issue_stage(n);
@@ -423,9 +426,9 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_stream_kernel(MlaArgs a) {
         for (int ht = 0; ht < HT; ++ht)
           pf[ht] = __builtin_bit_cast(f16x8_t, *(const uint4*)(sP + (ht * 16 + i16) * kPRow + 16 * g));
         const lds_char_t* lbuf = (const lds_char_t*)((lds_void_t*)buf);
-        uint2 vr[8][2];
+        uint2 vr[NT][2];
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int h = 0; h < 2; ++h)
             vr[nt][h] = __builtin_bit_cast(
@@ -433,7 +436,7 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_stream_kernel(MlaArgs a) {
                            (lds_s16x4_t*)(lbuf + v_off[h][nt & 3] + 128 * (nt >> 2))));
         sched_fence();
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
           const f16x8_t vf = __builtin_bit_cast(
               f16x8_t, uint4{bf16x2_to_f16x2(vr[nt][0].x), bf16x2_to_f16x2(vr[nt][0].y),
                              bf16x2_to_f16x2(vr[nt][1].x), bf16x2_to_f16x2(vr[nt][1].y)});
@@ -453,7 +456,7 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_stream_kernel(MlaArgs a) {
         for (int ht = 0; ht < HT; ++ht) {
           const float4 al = alv[ht];
 #pragma unroll
-          for (int nt = 0; nt < 8; ++nt) {
+          for (int nt = 0; nt < NT; ++nt) {
             o[ht][nt][0] *= al.x;
             o[ht][nt][1] *= al.y;
             o[ht][nt][2] *= al.z;
@@ -485,9 +488,9 @@ hipError_t launch_mla_stream(const MlaArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)(a.Hq / hpu * a.chunks));
   if (hpu == 64)
-    hipLaunchKernelGGL((mla_stream_kernel<4, NBUF>), grid, dim3(kMThreads), 0, s, a);
+    hipLaunchKernelGGL((mla_stream_kernel<4, 8, NBUF>), grid, dim3(8 * kWave), 0, s, a);
   else
-    hipLaunchKernelGGL((mla_stream_kernel<2, NBUF>), grid, dim3(kMThreads), 0, s, a);
+    hipLaunchKernelGGL((mla_stream_kernel<2, 4, NBUF>), grid, dim3(4 * kWave), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   DecodeArgs m{};
