@@ -473,6 +473,328 @@ __global__ __launch_bounds__(NW * kWave, 1) void mla_stream_kernel(MlaArgs a) {
   wait_vm<0>();
 }
 
+// Role-split variant for 64-head groups, 8 waves: waves 0-3 ("scorers") take stage n - scores
+// for one 16-head tile over all 32 tokens, the online softmax, P into LDS - while waves 4-7
+// ("accumulators") run p.V of stage n - 1 for 128 output dims each and copy the stages
+// HBM -> LDS.  Each SIMD holds one wave of each kind, so score and p.V products overlap, and
+// there is one workgroup barrier per stage.  P and the rescale factors are double-buffered by
+// stage parity; the copy of stage n + NBUF - 2 reuses the buffer of stage n - 2, which both
+// kinds of wave are done with by the barrier of iteration n.
+template <int NBUF>
+__global__ __launch_bounds__(8 * kWave, 1) void mla_split_kernel(MlaArgs a) {
+  constexpr int THREADS = 8 * kWave;
+  constexpr int HT = 4, HPU = 64;  // head tiles and heads per workgroup
+  constexpr int DPW = 128, NT = 8; // accumulator: output dims, p.V products per head tile
+  static_assert(NBUF >= 4, "two stages in flight");
+  __shared__ __attribute__((aligned(16))) uint8_t sbuf[NBUF * kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sP[2][HPU * kPRow];
+  __shared__ __attribute__((aligned(16))) float sAlpha[2][HPU];
+  static_assert((kMaxMlaSeqs + 1 + THREADS) * 4 <= NBUF * kStageBytes, "prefix scratch");
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
+  const bool scorer = w < 4;
+  const int r4 = w & 3;  // head tile (scorer) or output-dim slice (accumulator)
+  const int i16 = lane & 15, g = lane >> 4;
+  const int B = a.B, Hq = a.Hq, HG = Hq / HPU, C = a.chunks;
+  const int cap = a.max_blocks * kBlock;
+
+  // ---- stages per sequence and their exclusive prefix (scratch in the stage buffers)
+  int* s_pre = (int*)sbuf;
+  int* s_sum = s_pre + kMaxMlaSeqs + 1;
+  auto nstages = [&](int bi) {
+    int L = a.context_lens[bi];
+    L = L < 0 ? 0 : (L > cap ? cap : L);
+    return (L + kStage - 1) / kStage;
+  };
+  {
+    const int per = (B + THREADS - 1) / THREADS;
+    int local = 0;
+    for (int i = 0; i < per; ++i)
+      if (tid * per + i < B) local += nstages(tid * per + i);
+    s_sum[tid] = local;
+    __syncthreads();
+    for (int off = 1; off < THREADS; off <<= 1) {
+      const int v = tid >= off ? s_sum[tid - off] : 0;
+      __syncthreads();
+      s_sum[tid] += v;
+      __syncthreads();
+    }
+    int run = tid == 0 ? 0 : s_sum[tid - 1];
+    for (int i = 0; i < per; ++i) {
+      const int bi = tid * per + i;
+      if (bi < B) {
+        s_pre[bi] = run;
+        run += nstages(bi);
+      }
+    }
+    if (tid == 0) s_pre[B] = s_sum[THREADS - 1];
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      for (int i = tid; i <= B; i += THREADS) a.ws_prefix[i] = s_pre[i];
+      write_segment_ranges(a.ws_seg, s_pre, B, 1, C, tid, THREADS);
+    }
+  }
+
+  // ---- this workgroup's head group and chunk (head groups of a chunk on one XCD)
+  const int T = __builtin_amdgcn_readfirstlane(s_pre[B]);
+  const int x = blockIdx.x, xcd = x & 7, kx = x >> 3;
+  const int hg = kx % HG, ch = (kx / HG) * 8 + xcd;
+  const long long tb = (long long)T * ch / C, te = (long long)T * (ch + 1) / C;
+  const int ns = (int)min(te - tb, (long long)kMaxChunkStages);
+
+  // ---- per-stage first token (pool row index) and valid-token count | sequence << 6,
+  // two stages per lane
+  uint32_t row_l[2] = {0, 0};
+  int info_l[2] = {0, 0};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = kWave * j + lane;
+    if (n < ns) {
+      const int t = (int)(tb + n);
+      int lo = 0, hi = B - 1;  // last sequence whose first stage is <= t
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_pre[mid] <= t) lo = mid;
+        else hi = mid - 1;
+      }
+      const int js = t - s_pre[lo];
+      int L = a.context_lens[lo];
+      L = L < 0 ? 0 : (L > cap ? cap : L);
+      const int phys = a.block_table[(size_t)lo * a.max_blocks + js / 2];
+      const bool ok = (unsigned)phys < (unsigned)a.num_blocks;
+      row_l[j] = (uint32_t)(ok ? phys : 0) * kBlock + (js & 1) * kStage;
+      info_l[j] = (ok ? min(kStage, L - js * kStage) : 0) | (lo << 6);
+    }
+  }
+  uint64_t starts[2];  // stages that open a new piece
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = kWave * j + lane;
+    const int sq = info_l[j] >> 6;
+    int prev = __shfl_up(sq, 1);
+    if (lane == 0) prev = j ? __builtin_amdgcn_readlane(info_l[0], kWave - 1) >> 6 : -1;
+    starts[j] = __builtin_amdgcn_ballot_w64(n < ns && sq != prev);
+  }
+  auto stage_info = [&](int n) {
+    return __builtin_amdgcn_readlane(n >> 6 ? info_l[1] : info_l[0], n & (kWave - 1));
+  };
+  auto opens_piece = [&](int n) {  // n < ns
+    return ((n >> 6 ? starts[1] : starts[0]) >> (n & (kWave - 1))) & 1;
+  };
+  auto stage_src = [&](int n) -> i32x4_t {
+    if (n >= ns) return rsrc_words(a.kv_pool, 0);
+    const uint32_t row =
+        (uint32_t)__builtin_amdgcn_readlane((int)(n >> 6 ? row_l[1] : row_l[0]), n & (kWave - 1));
+    const int valid = stage_info(n) & 63;
+    return rsrc_words((const uint8_t*)a.kv_pool + (uint64_t)row * kRow, valid * kRow);
+  };
+
+  // The prefix scratch is dead from here on; clear the stage buffers once so that rows a
+  // stage does not load hold zeros or earlier valid rows, never garbage.
+  __syncthreads();
+  for (int i = tid; i < NBUF * kStageBytes / 16; i += THREADS)
+    *(uint4*)(sbuf + 16 * i) = uint4{0, 0, 0, 0};
+  __syncthreads();
+  if (ns <= 0) return;
+
+  // ---- LDS-direct stage copies by the accumulators: load j of accumulator r4 fills bytes
+  // [1024 (9 r4 + j), +1024) of the buffer (row t, permuted chunk p' as in mla_stream_kernel)
+  uint32_t dma_off[kDmaPerWave];
+#pragma unroll
+  for (int j = 0; j < kDmaPerWave; ++j) {
+    const int c = (r4 * kDmaPerWave + j) * kWave + lane;
+    const int t = c / kRowChunks, pp = c % kRowChunks;
+    dma_off[j] = (uint32_t)(16 * (t * kRowChunks + (pp ^ row_swizzle(t))));
+  }
+  const uint32_t sbuf_lds = (uint32_t)(uintptr_t)(lds_void_t*)sbuf;
+  auto issue_stage = [&](int n) {
+    if (scorer) return;
+    const i32x4_t src = stage_src(n);
+    const uint32_t base = sbuf_lds + (n % NBUF) * kStageBytes + r4 * kDmaPerWave * 1024;
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) lds_copy16(src, dma_off[j], base + j * 1024);
+  };
+
+  // ---- scorer: K (A operand) for token tile tt, chunk 4 ks + g -> even / odd ks offsets
+  int k_off[2][2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int t = tt * 16 + i16;
+    const int xm = g ^ row_swizzle(t);
+    k_off[tt][0] = 16 * (t * kRowChunks + xm);
+    k_off[tt][1] = 16 * (t * kRowChunks + (xm ^ 4));
+  }
+  // ---- accumulator: V (B operand, transposed reads) for dims 128 r4 + 16 nt + ...
+  int v_off[2][4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = 8 * g + 4 * h + (i16 >> 2);
+    const int qd = (i16 & 3) >> 1, half8 = 8 * (i16 & 1);
+#pragma unroll
+    for (int n4 = 0; n4 < 4; ++n4)
+      v_off[h][n4] = 16 * (t * kRowChunks + 16 * r4 + ((2 * n4 + qd) ^ row_swizzle(t))) + half8;
+  }
+
+  const float cscale = a.scale * kLog2e;
+  auto row0_of = [&](int sq) { return ((size_t)ch + sq) * Hq + (size_t)hg * HPU; };
+
+  // Each kind of wave runs its own loop (so that its state is all the compiler keeps live);
+  // both pass the same ns + 1 workgroup barriers.  At iteration n: stage n has landed (the
+  // accumulators' copies of it are older than the newest NBUF - 3 stages'), P and alpha of
+  // stage n - 1 are in LDS, and every wave is done with the buffer of stage n - 2, which the
+  // copy issued next overwrites.
+  if (scorer) {
+    bf16x8_t qf[kDqk / 32];  // q of head r4 * 16 + i16, this lane's dims
+    float m_run = kNegInf, l_part = 0.f;
+    int seq = -1;            // sequence of the open piece
+    auto flush_ml = [&]() {  // m and l of the open piece (slot ch + seq)
+      const float l_head = group_sum4(l_part);
+      if (g == 0) {
+        a.ws_m[row0_of(seq) + r4 * 16 + i16] = m_run;
+        a.ws_l[row0_of(seq) + r4 * 16 + i16] = l_head;
+      }
+    };
+    for (int n = 0; n <= ns; ++n) {
+      barrier_vm<kDmaPerWave * (NBUF - 3)>();
+      if (n == ns) break;
+      const int info = stage_info(n), valid = info & 63, sq = info >> 6;
+      if (sq != seq) {
+        if (seq >= 0) flush_ml();
+        seq = sq;
+        const uint8_t* qrow =
+            (const uint8_t*)(a.q + ((size_t)sq * Hq + (size_t)hg * HPU + r4 * 16 + i16) * kDqk);
+#pragma unroll
+        for (int ks = 0; ks < kDqk / 32; ++ks)
+          qf[ks] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(qrow + ks * 64 + 16 * g));
+        wait_vm<0>();  // scorers issue no stage copies: this only waits for q
+        // O is not cleared: with the running max back at -inf, the piece's first stage with
+        // a valid token sends alpha = 2^(-inf) = 0, which clears the accumulators' rows.
+        m_run = kNegInf;
+        l_part = 0.f;
+      }
+      const uint8_t* buf = sbuf + (n % NBUF) * kStageBytes;
+      // S^T = K Q^T for both token tiles (two independent accumulation chains)
+      f32x4_t s[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int k0 = 0; k0 < kDqk / 32; k0 += 6) {
+        bf16x8_t kf[2][6];
+#pragma unroll
+        for (int ks = 0; ks < 6; ++ks)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+            kf[tt][ks] = __builtin_bit_cast(
+                bf16x8_t, *(const uint4*)(buf + k_off[tt][(k0 + ks) & 1] + 128 * ((k0 + ks) >> 1)));
+#pragma unroll
+        for (int ks = 0; ks < 6; ++ks)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) s[tt] = mfma_bf16(kf[tt][ks], qf[k0 + ks], s[tt]);
+      }
+      // online softmax (log2 domain): lane holds tokens tt * 16 + 4 g + r of head i16
+      float sv[8];
+      float mt = kNegInf;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tok = tt * 16 + 4 * g + r;
+          const float v = tok < valid ? s[tt][r] * cscale : kNegInf;
+          sv[tt * 4 + r] = v;
+          mt = fmaxf(mt, v);
+        }
+      mt = group_max4(mt);
+      float alpha = 1.f;
+      if (wave_any(mt > m_run + kSlack)) {
+        const float m_new = fmaxf(m_run, mt);
+        alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+        l_part *= alpha;
+        m_run = m_new;
+      }
+      if (g == 0) sAlpha[n & 1][r4 * 16 + i16] = alpha;
+      const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+      uint8_t* prow = sP[n & 1] + (r4 * 16 + i16) * kPRow;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const uint32_t p01 = pack_f16(fast_exp2(sv[tt * 4 + 0] - m_use), fast_exp2(sv[tt * 4 + 1] - m_use));
+        const uint32_t p23 = pack_f16(fast_exp2(sv[tt * 4 + 2] - m_use), fast_exp2(sv[tt * 4 + 3] - m_use));
+        l_part = dot2h(p01, kOnesF16x2, l_part);
+        l_part = dot2h(p23, kOnesF16x2, l_part);
+        *(uint2*)(prow + (tt * 16 + 4 * g) * 2) = uint2{p01, p23};
+      }
+    }
+    flush_ml();
+  } else {
+    f32x4_t o[HT][NT];  // O^T rows 4 g + r of each head tile, dims 128 r4 + 16 nt + i16
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) o[ht][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};  // finite for alpha = 0
+    for (int n = 0; n < NBUF - 2; ++n) issue_stage(n);
+    for (int n = 0; n <= ns; ++n) {
+      barrier_vm<kDmaPerWave * (NBUF - 3)>();
+      issue_stage(n + NBUF - 2);
+      if (n == 0) continue;
+      const int pn = n - 1;
+      // scale O's rows by their heads' alpha when some head's running max moved (rare)
+      float4 alv[HT];
+      bool anyr = false;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        alv[ht] = *(const float4*)&sAlpha[pn & 1][ht * 16 + 4 * g];
+        anyr |= alv[ht].x != 1.f || alv[ht].y != 1.f || alv[ht].z != 1.f || alv[ht].w != 1.f;
+      }
+      if (wave_any(anyr)) {
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+          const float4 al = alv[ht];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            o[ht][nt][0] *= al.x;
+            o[ht][nt][1] *= al.y;
+            o[ht][nt][2] *= al.z;
+            o[ht][nt][3] *= al.w;
+          }
+        }
+      }
+      f16x8_t pf[HT];
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+        pf[ht] = __builtin_bit_cast(f16x8_t, *(const uint4*)(sP[pn & 1] + (ht * 16 + i16) * kPRow + 16 * g));
+      const lds_char_t* lbuf = (const lds_char_t*)((lds_void_t*)(sbuf + (pn % NBUF) * kStageBytes));
+      uint2 vr[NT][2];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          vr[nt][h] = __builtin_bit_cast(
+              uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                         (lds_s16x4_t*)(lbuf + v_off[h][nt & 3] + 128 * (nt >> 2))));
+      sched_fence();
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const f16x8_t vf = __builtin_bit_cast(
+            f16x8_t, uint4{bf16x2_to_f16x2(vr[nt][0].x), bf16x2_to_f16x2(vr[nt][0].y),
+                           bf16x2_to_f16x2(vr[nt][1].x), bf16x2_to_f16x2(vr[nt][1].y)});
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) o[ht][nt] = mfma_f16(pf[ht], vf, o[ht][nt]);
+      }
+      if (n == ns || opens_piece(n)) {  // stage pn closed its piece: write o (slot ch + seq)
+        const size_t row0 = row0_of(stage_info(pn) >> 6);
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              a.ws_o[(row0 + ht * 16 + 4 * g + r) * kDv + DPW * r4 + 16 * nt + i16] = o[ht][nt][r];
+      }
+    }
+  }
+  // Copies of stages past the end may still be in flight: they must land before this
+  // workgroup's LDS can be handed to another one.
+  wait_vm<0>();
+}
+
 // 64 heads per workgroup (two waves' worth of p.V accumulators per wave) where Hq allows,
 // else 32.
 int mla_stream_heads_per_group(int Hq) {
@@ -488,7 +810,7 @@ hipError_t launch_mla_stream(const MlaArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)(a.Hq / hpu * a.chunks));
   if (hpu == 64)
-    hipLaunchKernelGGL((mla_stream_kernel<4, 8, NBUF>), grid, dim3(8 * kWave), 0, s, a);
+    hipLaunchKernelGGL((mla_split_kernel<NBUF>), grid, dim3(8 * kWave), 0, s, a);
   else
     hipLaunchKernelGGL((mla_stream_kernel<2, 4, NBUF>), grid, dim3(4 * kWave), 0, s, a);
   hipError_t e = hipGetLastError();
