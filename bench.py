@@ -88,6 +88,8 @@ def traffic_for(workload_name, kind):
 
 def kernel_label(w, pkv, ps):
     if w.kind == "mla":
+        if ps == 0 and w.Hq % 64 == 0 and w.Hq <= 128:
+            return "pkv_paged_decode_attn_mla call, balanced mode (mla_split_kernel + stream_merge_kernel<512>)"
         if ps == 0 and w.Hq % 32 == 0 and w.Hq <= 128:
             return "pkv_paged_decode_attn_mla call, balanced mode (mla_stream_kernel + stream_merge_kernel<512>)"
         return "pkv_paged_decode_attn_mla call, partitioned (mla_decode_kernel + partition_merge_kernel<512>)"
