@@ -512,15 +512,36 @@ __global__ __launch_bounds__(8 * kWave, 1) void mla_split_kernel(MlaArgs a) {
   const int B = a.B, Hq = a.Hq, HG = Hq / HPU, C = a.chunks;
   const int cap = a.max_blocks * kBlock;
 
-  // ---- stages per sequence and their exclusive prefix (scratch in the stage buffers)
+  // ---- stages per sequence and their exclusive prefix.  Up to 64 sequences every wave
+  // scans them in registers (lane i: sequence i), so that no workgroup barrier or LDS round
+  // trip sits between the context lengths and the first stage copies; more sequences take a
+  // workgroup-wide scan with scratch in the stage buffers.
   int* s_pre = (int*)sbuf;
   int* s_sum = s_pre + kMaxMlaSeqs + 1;
-  auto nstages = [&](int bi) {
-    int L = a.context_lens[bi];
-    L = L < 0 ? 0 : (L > cap ? cap : L);
-    return (L + kStage - 1) / kStage;
-  };
-  {
+  auto clamp_len = [&](int L) { return L < 0 ? 0 : (L > cap ? cap : L); };
+  auto nstages = [&](int bi) { return (clamp_len(a.context_lens[bi]) + kStage - 1) / kStage; };
+  const bool wave_scan = B <= kWave;
+  int pre_l = 0, len_l = 0;  // register scan: sequence `lane`'s first stage and length
+  int T;
+  if (wave_scan) {
+    len_l = lane < B ? clamp_len(a.context_lens[lane]) : 0;
+    const int ns_l = (len_l + kStage - 1) / kStage;
+    int incl = ns_l;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    pre_l = incl - ns_l;
+    T = __builtin_amdgcn_readlane(incl, kWave - 1);
+    if (blockIdx.x == 0 && w == 0) {
+      if (lane < B) {
+        a.ws_prefix[lane] = pre_l;
+        segment_range(pre_l, ns_l, T, C, a.ws_seg + 2 * lane);
+      }
+      if (lane == 0) a.ws_prefix[B] = T;
+    }
+  } else {
     const int per = (B + THREADS - 1) / THREADS;
     int local = 0;
     for (int i = 0; i < per; ++i)
@@ -547,10 +568,10 @@ __global__ __launch_bounds__(8 * kWave, 1) void mla_split_kernel(MlaArgs a) {
       for (int i = tid; i <= B; i += THREADS) a.ws_prefix[i] = s_pre[i];
       write_segment_ranges(a.ws_seg, s_pre, B, 1, C, tid, THREADS);
     }
+    T = __builtin_amdgcn_readfirstlane(s_pre[B]);
   }
 
   // ---- this workgroup's head group and chunk (head groups of a chunk on one XCD)
-  const int T = __builtin_amdgcn_readfirstlane(s_pre[B]);
   const int x = blockIdx.x, xcd = x & 7, kx = x >> 3;
   const int hg = kx % HG, ch = (kx / HG) * 8 + xcd;
   const long long tb = (long long)T * ch / C, te = (long long)T * (ch + 1) / C;
@@ -563,17 +584,29 @@ __global__ __launch_bounds__(8 * kWave, 1) void mla_split_kernel(MlaArgs a) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int n = kWave * j + lane;
-    if (n < ns) {
-      const int t = (int)(tb + n);
-      int lo = 0, hi = B - 1;  // last sequence whose first stage is <= t
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_pre[mid] <= t) lo = mid;
-        else hi = mid - 1;
+    const int t = (int)(tb + min(n, max(ns - 1, 0)));
+    int lo = 0, js = 0, L = 0;  // last sequence whose first stage is <= t
+    if (wave_scan) {            // all lanes take part in the shuffles
+#pragma unroll
+      for (int step = kWave / 2; step >= 1; step >>= 1) {
+        const int cand = lo + step;
+        const int v = __shfl(pre_l, cand < B ? cand : 0);
+        if (cand < B && v <= t) lo = cand;
       }
-      const int js = t - s_pre[lo];
-      int L = a.context_lens[lo];
-      L = L < 0 ? 0 : (L > cap ? cap : L);
+      js = t - __shfl(pre_l, lo);
+      L = __shfl(len_l, lo);
+    }
+    if (n < ns) {
+      if (!wave_scan) {
+        int hi = B - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_pre[mid] <= t) lo = mid;
+          else hi = mid - 1;
+        }
+        js = t - s_pre[lo];
+        L = clamp_len(a.context_lens[lo]);
+      }
       const int phys = a.block_table[(size_t)lo * a.max_blocks + js / 2];
       const bool ok = (unsigned)phys < (unsigned)a.num_blocks;
       row_l[j] = (uint32_t)(ok ? phys : 0) * kBlock + (js & 1) * kStage;
@@ -605,7 +638,7 @@ __global__ __launch_bounds__(8 * kWave, 1) void mla_split_kernel(MlaArgs a) {
 
   // The prefix scratch is dead from here on; clear the stage buffers once so that rows a
   // stage does not load hold zeros or earlier valid rows, never garbage.
-  __syncthreads();
+  if (!wave_scan) __syncthreads();
   for (int i = tid; i < NBUF * kStageBytes / 16; i += THREADS)
     *(uint4*)(sbuf + 16 * i) = uint4{0, 0, 0, 0};
   __syncthreads();
@@ -669,7 +702,21 @@ __global__ __launch_bounds__(8 * kWave, 1) void mla_split_kernel(MlaArgs a) {
   if (scorer) {
     bf16x8_t qf[kDqk / 32];  // q of head r4 * 16 + i16, this lane's dims
     float m_run = kNegInf, l_part = 0.f;
-    int seq = -1;            // sequence of the open piece
+    auto load_q = [&](int sq) {  // q of head r4 * 16 + i16 of sequence sq, no wait
+      const uint8_t* qrow =
+          (const uint8_t*)(a.q + ((size_t)sq * Hq + (size_t)hg * HPU + r4 * 16 + i16) * kDqk);
+#pragma unroll
+      for (int ks = 0; ks < kDqk / 32; ++ks) {
+        const int chunk = ks < 16 ? ks + 16 * g : 64 + 4 * (ks - 16) + tail_g;
+        qf[ks] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(qrow + 16 * chunk));
+      }
+    };
+    // The first piece's q is requested before the first barrier, alongside the first stage
+    // copies.  O is not cleared at a piece start: with the running max back at -inf, the
+    // piece's first stage with a valid token sends alpha = 2^(-inf) = 0, which clears the
+    // accumulators' rows.
+    int seq = stage_info(0) >> 6;  // sequence of the open piece
+    load_q(seq);
     auto flush_ml = [&]() {  // m and l of the open piece (slot ch + seq)
       const float l_head = group_sum4(l_part);
       if (g == 0) {
@@ -682,18 +729,10 @@ __global__ __launch_bounds__(8 * kWave, 1) void mla_split_kernel(MlaArgs a) {
       if (n == ns) break;
       const int info = stage_info(n), valid = info & 63, sq = info >> 6;
       if (sq != seq) {
-        if (seq >= 0) flush_ml();
+        flush_ml();
         seq = sq;
-        const uint8_t* qrow =
-            (const uint8_t*)(a.q + ((size_t)sq * Hq + (size_t)hg * HPU + r4 * 16 + i16) * kDqk);
-#pragma unroll
-        for (int ks = 0; ks < kDqk / 32; ++ks) {
-          const int chunk = ks < 16 ? ks + 16 * g : 64 + 4 * (ks - 16) + tail_g;
-          qf[ks] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(qrow + 16 * chunk));
-        }
+        load_q(sq);
         wait_vm<0>();  // scorers issue no stage copies: this only waits for q
-        // O is not cleared: with the running max back at -inf, the piece's first stage with
-        // a valid token sends alpha = 2^(-inf) = 0, which clears the accumulators' rows.
         m_run = kNegInf;
         l_part = 0.f;
       }

@@ -150,21 +150,24 @@ __device__ __forceinline__ int chunk_of(long long t, long long T, int C) {
 // For the merge kernel, per segment s = g * B + b: the first range holding its units and the
 // number of ranges it spans (0 for a sequence without units).  pre[0..B] is the exclusive
 // prefix of units per sequence; threads tid, tid + nthreads, ... of one workgroup write.
+// First range and number of ranges of a segment of nb units starting at unit `first`.
+__device__ __forceinline__ void segment_range(long long first, int nb, long long T, int C,
+                                              int32_t* out) {
+  int c0 = 0, n = 0;
+  if (nb > 0) {
+    c0 = chunk_of(first, T, C);
+    n = chunk_of(first + nb - 1, T, C) - c0 + 1;
+  }
+  out[0] = c0;
+  out[1] = n;
+}
 __device__ __forceinline__ void write_segment_ranges(int32_t* ws_seg, const int* pre, int B,
                                                      int H, int C, int tid, int nthreads) {
   const int T_head = pre[B];
   const long long T = (long long)H * T_head;
   for (int sg = tid; sg < H * B; sg += nthreads) {
     const int g = sg / B, b = sg - g * B;
-    const int nb = pre[b + 1] - pre[b];
-    int c0 = 0, n = 0;
-    if (nb > 0) {
-      const long long first = (long long)g * T_head + pre[b];
-      c0 = chunk_of(first, T, C);
-      n = chunk_of(first + nb - 1, T, C) - c0 + 1;
-    }
-    ws_seg[2 * sg] = c0;
-    ws_seg[2 * sg + 1] = n;
+    segment_range((long long)g * T_head + pre[b], pre[b + 1] - pre[b], T, C, ws_seg + 2 * sg);
   }
 }
 

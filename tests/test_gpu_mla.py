@@ -86,6 +86,18 @@ def test_mla_balanced_one_long_sequence():
     assert_close(got, oracle_decode(w), "bf16", "mla balanced, one 8192-token sequence")
 
 
+@pytest.mark.parametrize("B", [64, 65])
+def test_mla_balanced_batch_scan_boundary(B):
+    """64 sequences are the most the 64-head kernel scans in registers; 65 take the
+    workgroup-wide scan.  Both must give the same stage map and merge bookkeeping."""
+    torch = torch_cuda()
+    w = make_workload("mla", seed=16 + B, B=B, lens=("uniform", 0, 300))
+    w.context_lens[B - 1] = 0
+    log(f"[mla] balanced B={B} lens<=300 (zeros: {int((w.context_lens == 0).sum())})")
+    assert_close(gpu_decode(torch, w, partition_size=0), oracle_decode(w), "bf16",
+                 f"mla balanced B={B}")
+
+
 @pytest.mark.parametrize("hq", [32, 96])
 def test_mla_balanced_head_groups(hq):
     torch = torch_cuda()
