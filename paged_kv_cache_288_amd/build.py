@@ -15,6 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpkv.so")
 READ_CEILING = os.path.join(HERE, "read_ceiling")   # standalone bandwidth probe
+LDS_PROBE = os.path.join(HERE, "lds_probe")         # standalone LDS bank probe
 ARCH = "gfx950"
 
 SOURCES = ["pkv_api.hip", "kv_append.hip", "gqa_decode.hip", "gqa_stream.hip", "mla_decode.hip",
@@ -61,13 +62,15 @@ def build(isa=False, verbose=True):
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
-    cmd = [HIPCC, *FLAGS, os.path.join(CSRC, "read_ceiling.hip"), "-o", READ_CEILING + ".tmp"]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for read_ceiling.hip:\n{r.stderr}")
-    os.replace(READ_CEILING + ".tmp", READ_CEILING)
+    for exe in (READ_CEILING, LDS_PROBE):
+        src = os.path.basename(exe) + ".hip"
+        cmd = [HIPCC, *FLAGS, os.path.join(CSRC, src), "-o", exe + ".tmp"]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        os.replace(exe + ".tmp", exe)
     if verbose:
-        print(f"built {LIB} and {READ_CEILING}")
+        print(f"built {LIB}, {READ_CEILING} and {LDS_PROBE}")
     return LIB
 
 
