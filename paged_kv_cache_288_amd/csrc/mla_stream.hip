@@ -755,6 +755,7 @@ __global__ __launch_bounds__(8 * kWave, 1) void mla_split_kernel(MlaArgs a) {
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) s[tt] = mfma_bf16(kf[tt][ks], qf[k0 + ks], s[tt]);
       }
+
       // online softmax (log2 domain): lane holds tokens tt * 16 + 4 g + r of head i16.  The
       // maximum is taken over the raw scores and scaled once (cscale > 0).
       float sv[8];
@@ -833,11 +834,21 @@ __global__ __launch_bounds__(8 * kWave, 1) void mla_split_kernel(MlaArgs a) {
               uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                          (lds_s16x4_t*)(lbuf + v_off[h][nt & 3] + 128 * (nt >> 2))));
       sched_fence();
+      // widen all of V first, in place, then issue the 32 products back to back (widening
+      // slice by slice into shared registers makes each slice wait for the products
+      // still reading the previous one)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          vr[nt][h].x = bf16x2_to_f16x2(vr[nt][h].x);
+          vr[nt][h].y = bf16x2_to_f16x2(vr[nt][h].y);
+        }
+      sched_fence();
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const f16x8_t vf = __builtin_bit_cast(
-            f16x8_t, uint4{bf16x2_to_f16x2(vr[nt][0].x), bf16x2_to_f16x2(vr[nt][0].y),
-                           bf16x2_to_f16x2(vr[nt][1].x), bf16x2_to_f16x2(vr[nt][1].y)});
+            f16x8_t, uint4{vr[nt][0].x, vr[nt][0].y, vr[nt][1].x, vr[nt][1].y});
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) o[ht][nt] = mfma_f16(pf[ht], vf, o[ht][nt]);
       }
