@@ -152,6 +152,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--flush", action="store_true",
                     help="write 512 MiB of scratch before every step (outside the call's events)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step's append and attention call as captured graphs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (to scale memory counters)")
     args = ap.parse_args()
@@ -220,6 +222,27 @@ def main():
         if ev is not None:
             ev[1].record()
 
+    if args.graph:
+        # all cache copies' steps (append + attention each) captured as one graph, replayed
+        # once per `layers` steps, as a model step over several layers would be; the
+        # replays run the same kernels as the eager steps
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            pkv.graph_begin()
+            for i in range(args.layers):
+                pkv.kv_append(kps[i], vps[i], nk, nv, slots, kv_dtype=w.kv_dtype)
+                attend(kps[i], vps[i])
+            graph = pkv.graph_end()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        if args.steps % args.layers or args.warmup % args.layers or args.flush:
+            sys.exit("--graph needs --steps and --warmup multiples of --layers, and no --flush")
+
+        def step(i, ev=None):  # noqa: F811  (the graph-replay step)
+            if i % args.layers == 0:
+                graph.launch()
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -234,7 +257,10 @@ def main():
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
-    call_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    if args.graph:  # no events inside a replay: the step time (append + attention) stands in
+        call_ms = np.full(args.steps, total_ms / args.steps)
+    else:
+        call_ms = np.array([a.elapsed_time(b) for a, b in evs])
     ms_per_step = total_ms / args.steps
 
     if args.copy_calibration:
@@ -290,7 +316,7 @@ def main():
             "partition_size": int(pkv.decode_partition_size(w.B, w.Hkv, w.max_context_len, ps))
             if w.kind != "mla" else ps,
             "kv_bytes_per_step": kvb, "flush_between_steps": bool(args.flush),
-            "cache_copies_rotated": args.layers,
+            "cache_copies_rotated": args.layers, "graph_replay": bool(args.graph),
         },
         "decode_tokens_per_s": round(w.B / (ms_per_step * 1e-3), 1),
         "hbm_peak_frac_step": round(kvb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -190,6 +190,29 @@ pkv_status pkv_paged_decode_attn_mla(float* out, const void* q, const void* kv_p
                                      float scale, int32_t partition_size, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
+/* ---- Graph capture of a decode step ("GPU推理深度拆解：KV Cache视角", "算子优化要点":
+ * replaying a captured step removes the per-kernel launch overhead, at the price of static
+ * shapes and addresses, so steps are padded to the nearest bucket).
+ *
+ * pkv_graph_begin starts capturing what is enqueued on `stream` (not the null stream) from
+ * this thread; the library calls made on that stream until pkv_graph_end are recorded, not
+ * run.  pkv_graph_end stops the capture and instantiates it into *graph (caller-owned,
+ * released by pkv_graph_destroy).  pkv_graph_launch enqueues one replay on `stream`.
+ *
+ * A replay runs the recorded kernels with the pointers and sizes they were given: the
+ * caller updates the buffers' contents in place (q, new rows, slot mapping, block table,
+ * context lengths) between replays and keeps every buffer and the workspace alive until
+ * the graph is destroyed.  The library's calls record kernel launches only (no memory set
+ * or copy nodes), so a replay needs no clearing.  Errors: PKV_ERR_NULL for a missing
+ * stream or graph pointer, PKV_ERR_HIP when the runtime rejects the capture (a library call
+ * that fails while capturing returns its own status; the capture must still be ended and
+ * the resulting graph destroyed). */
+typedef struct pkv_graph* pkv_graph_t;
+pkv_status pkv_graph_begin(void* stream);
+pkv_status pkv_graph_end(void* stream, pkv_graph_t* graph);
+pkv_status pkv_graph_launch(pkv_graph_t graph, void* stream);
+pkv_status pkv_graph_destroy(pkv_graph_t graph);
+
 #ifdef __cplusplus
 }
 #endif

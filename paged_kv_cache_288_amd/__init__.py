@@ -13,11 +13,15 @@ import os
 __all__ = [
     "PKV_BF16", "PKV_FP8_E4M3", "PkvError", "library_path", "load_library",
     "abi_version", "kv_append", "decode_partition_size", "decode_workspace_bytes",
-    "paged_decode_attn", "mla_workspace_bytes", "paged_decode_attn_mla",
+    "paged_decode_attn", "mla_workspace_bytes", "paged_decode_attn_mla", "Graph",
+    "graph_begin", "graph_end", "graph_launch", "graph_destroy",
 ]
 
 PKV_BF16 = 1
 PKV_FP8_E4M3 = 2
+# status codes (include/pkv.h)
+PKV_OK, PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_DTYPE, PKV_ERR_UNSUPPORTED = 0, -1, -2, -3, -4
+PKV_ERR_ALIGN, PKV_ERR_WORKSPACE, PKV_ERR_HIP = -5, -6, -7
 _DTYPES = {"bf16": PKV_BF16, "fp8": PKV_FP8_E4M3}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -42,6 +46,10 @@ _SIGNATURES = [
     ("pkv_paged_decode_attn_mla", _c_int32, [_p, _p, _p, _p, _p, _c_int32, _c_int32, _c_int32,
                                              _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
                                              ctypes.c_float, _c_int32, _p, _c_size, _p]),
+    ("pkv_graph_begin", _c_int32, [_p]),
+    ("pkv_graph_end", _c_int32, [_p, ctypes.POINTER(ctypes.c_void_p)]),
+    ("pkv_graph_launch", _c_int32, [_p, _p]),
+    ("pkv_graph_destroy", _c_int32, [_p]),
 ]
 EXPORTED = [name for name, _, _ in _SIGNATURES]
 
@@ -178,3 +186,55 @@ def paged_decode_attn_mla(out, q, kv_pool, block_table, context_lens, scale, max
         partition_size, _ptr(workspace), wsize, _stream(q.device))
     _check("pkv_paged_decode_attn_mla", st)
     return out
+
+
+class Graph:
+    """Library calls captured on a stream (pkv_graph_end), replayed by launch()."""
+
+    def __init__(self, handle, device):
+        self._handle = handle
+        self.device = device
+
+    def launch(self):
+        """Enqueue one replay on the device's current stream (pkv_graph_launch)."""
+        if self._handle is None:
+            raise RuntimeError("graph already destroyed")
+        _check("pkv_graph_launch",
+               load_library().pkv_graph_launch(self._handle, _stream(self.device)))
+
+    def destroy(self):
+        if self._handle is not None:
+            st = load_library().pkv_graph_destroy(self._handle)
+            self._handle = None
+            _check("pkv_graph_destroy", st)
+
+    def __del__(self):
+        if getattr(self, "_handle", None) is not None and _LIB is not None:
+            _LIB.pkv_graph_destroy(self._handle)
+            self._handle = None
+
+
+def graph_begin(device=None):
+    """Start capturing the device's current stream (pkv_graph_begin); it must not be the
+    default stream.  Calls made on it until graph_end are recorded, not run."""
+    import torch
+    device = torch.device("cuda") if device is None else torch.device(device)
+    _check("pkv_graph_begin", load_library().pkv_graph_begin(_stream(device)))
+
+
+def graph_end(device=None):
+    """Stop the capture started by graph_begin and instantiate it (pkv_graph_end)."""
+    import torch
+    device = torch.device("cuda") if device is None else torch.device(device)
+    handle = ctypes.c_void_p()
+    _check("pkv_graph_end", load_library().pkv_graph_end(_stream(device), ctypes.byref(handle)))
+    return Graph(handle, device)
+
+
+def graph_launch(graph):
+    graph.launch()
+
+
+def graph_destroy(graph):
+    graph.destroy()
+

@@ -1,7 +1,10 @@
 // C-ABI of the paged decode-attention library: argument validation, partition choice,
 // workspace sizing and dispatch to the kernel launchers.  Validation touches no HIP API,
-// so every error return happens before anything is enqueued.
+// so every error return happens before anything is enqueued.  Also the capture and replay
+// of decode steps as HIP graphs.
 #include <stdint.h>
+
+#include <new>
 
 #include "../../include/pkv.h"
 #include "pkv_launch.hpp"
@@ -82,13 +85,17 @@ int device_cus() {
 }
 
 // Balanced mode: one chunk per wave, two 4-wave workgroups per CU, and enough chunks that
-// none holds more than kMaxChunkTiles tiles even if every context were max_context_len.
+// none holds more than kMaxChunkTiles tiles even if every context were max_context_len;
+// never more chunks than that bound on the tiles (rounded up to 32), so that a small
+// batch is not spread over thousands of empty chunks the merge would walk.
 int32_t stream_chunks(int32_t B, int32_t Hkv, int32_t max_ctx) {
   const long long tmax = (long long)Hkv * B * ((max_ctx + 15) / 16);
   long long c = 8LL * device_cus();
+  if (tmax < c) c = tmax;
   const long long need = (tmax + kMaxChunkTiles - 1) / kMaxChunkTiles;
   if (need > c) c = need;
   c = (c + 31) / 32 * 32;
+  if (c < 32) c = 32;
   return c > (1LL << 30) ? -1 : (int32_t)c;
 }
 
@@ -102,15 +109,18 @@ size_t stream_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t ch
          round256((size_t)Hkv * B * 2 * sizeof(int32_t));
 }
 
-// Latent balanced mode: one 4-wave workgroup per CU, Hq / 32 head groups, chunks a
-// multiple of 8 and enough of them that none holds more than 128 stages of 32 tokens.
+// Latent balanced mode: one workgroup per CU, Hq / 32 or Hq / 64 head groups, chunks a
+// multiple of 8, enough of them that none holds more than 128 stages of 32 tokens, and no
+// more than the bound on the stages (rounded up to 8).
 int32_t mla_stream_chunks(int32_t B, int32_t Hq, int32_t max_ctx) {
   const long long hg = Hq / pkv::mla_stream_heads_per_group(Hq);
   const long long smax = (long long)B * ((max_ctx + 31) / 32);
   long long c = (device_cus() + hg - 1) / hg;
+  if (smax < c) c = smax;
   const long long need = (smax + 127) / 128;
   if (need > c) c = need;
   c = (c + 7) / 8 * 8;
+  if (c < 8) c = 8;
   return c > (1LL << 24) ? -1 : (int32_t)c;
 }
 
@@ -328,6 +338,49 @@ pkv_status pkv_paged_decode_attn_mla(float* out, const void* q, const void* kv_p
   return hip_status(pkv::launch_partition_merge(ws_m, ws_l, ws_o, context_lens, out, B, Hq, d_v,
                                                 ps, P, ctx,
                                                 max_blocks_per_seq * block_size, s));
+}
+
+struct pkv_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+pkv_status pkv_graph_begin(void* stream) {
+  if (!stream) return PKV_ERR_NULL;
+  return hip_status(hipStreamBeginCapture((hipStream_t)stream, hipStreamCaptureModeThreadLocal));
+}
+
+pkv_status pkv_graph_end(void* stream, pkv_graph_t* graph) {
+  if (!stream || !graph) return PKV_ERR_NULL;
+  *graph = nullptr;
+  hipGraph_t g = nullptr;
+  if (hipStreamEndCapture((hipStream_t)stream, &g) != hipSuccess || !g) return PKV_ERR_HIP;
+  hipGraphExec_t exec = nullptr;
+  if (hipGraphInstantiate(&exec, g, nullptr, nullptr, 0) != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return PKV_ERR_HIP;
+  }
+  pkv_graph* h = new (std::nothrow) pkv_graph{g, exec};
+  if (!h) {
+    (void)hipGraphExecDestroy(exec);
+    (void)hipGraphDestroy(g);
+    return PKV_ERR_HIP;
+  }
+  *graph = h;
+  return PKV_OK;
+}
+
+pkv_status pkv_graph_launch(pkv_graph_t graph, void* stream) {
+  if (!graph) return PKV_ERR_NULL;
+  return hip_status(hipGraphLaunch(graph->exec, (hipStream_t)stream));
+}
+
+pkv_status pkv_graph_destroy(pkv_graph_t graph) {
+  if (!graph) return PKV_OK;
+  const hipError_t e1 = hipGraphExecDestroy(graph->exec);
+  const hipError_t e2 = hipGraphDestroy(graph->graph);
+  delete graph;
+  return (e1 == hipSuccess && e2 == hipSuccess) ? PKV_OK : PKV_ERR_HIP;
 }
 
 }  // extern "C"

@@ -1,0 +1,141 @@
+"""Decode steps captured as a graph and replayed (paged_kv_cache_288_amd.graph.DecodeStep)
+against the same calls made eagerly.
+
+The last S positions of every sequence are poisoned with NaN in two copies of the pool;
+each step then appends the true row of the next position and attends with the context
+grown by one, once through the graph's replay and once eagerly with the same shapes.
+The replayed output and pool must equal the eager ones bit for bit at every step (same
+kernels, same inputs), with eager work and synchronisations between the replays; the
+last step, whose contexts are the full sequences, is also held to the oracle."""
+
+import numpy as np
+import pytest
+
+from gpu_common import (assert_close, bits_to_device, log, make_workload, oracle_decode,
+                        torch_cuda)
+
+S = 4  # decode steps replayed
+
+
+def _poison(pool_bits, w, kind):
+    nan = np.uint8(0x7F) if w.kv_dtype == "fp8" else np.uint16(0x7FC0)
+    p = pool_bits.copy()
+    for b in range(w.B):
+        for pos in range(int(w.context_lens[b]) - S, int(w.context_lens[b])):
+            phys, off = w.block_table[b, pos // w.bs], pos % w.bs
+            if kind == "mla":
+                p[phys, off] = nan
+            else:
+                p[phys, :, off] = nan
+    return p
+
+
+def _step_rows(w, kind, s):
+    """Rows, slots and context lengths of step s (0-based): position L_b - S + s."""
+    pos = w.context_lens.astype(np.int64) - S + s
+    phys = w.block_table[np.arange(w.B), pos // w.bs].astype(np.int64)
+    off = pos % w.bs
+    if kind == "mla":
+        k = w.k_pool[phys, off][:, None, :]
+        v = None
+    else:
+        k = w.k_pool[phys, :, off, :]
+        v = w.v_pool[phys, :, off, :]
+    return k, v, phys * w.bs + off, (pos + 1).astype(np.int32)
+
+
+def _run(w, kind):
+    torch = torch_cuda()
+    import paged_kv_cache_288_amd as pkv
+    from paged_kv_cache_288_amd.graph import DecodeStep, bucket_batch, bucket_context
+    assert int(w.context_lens.min()) > S
+    Bb, Cb = bucket_batch(w.B), bucket_context(w.max_context_len, w.bs)
+    log(f"[graph] {kind} B={w.B} -> bucket {Bb}, max ctx {w.max_context_len} -> {Cb}")
+    kp_g = bits_to_device(torch, _poison(w.k_pool, w, kind))
+    kp_e = kp_g.clone()
+    vp_g = vp_e = None
+    if w.v_pool is not None:
+        vp_g = bits_to_device(torch, _poison(w.v_pool, w, kind))
+        vp_e = vp_g.clone()
+    ks = None if w.k_scale is None else torch.from_numpy(w.k_scale).cuda()
+    vs = None if w.v_scale is None else torch.from_numpy(w.v_scale).cuda()
+    step = DecodeStep(kind, kp_g, vp_g, w.Hq, w.scale, Bb, Cb, kv_dtype=w.kv_dtype,
+                      k_scale=ks, v_scale=vs, d_v=w.d_v)
+    bt = torch.from_numpy(w.block_table.astype(np.int32)).cuda()
+    # the eager reference runs the bucket's padded shapes, as the capture does (the chunking
+    # of the balanced modes depends on the batch)
+    bt_pad = torch.zeros((Bb, step.max_blocks), dtype=torch.int32, device="cuda")
+    width = min(bt.shape[1], step.max_blocks)
+    bt_pad[:w.B, :width] = bt[:, :width]
+    out_e = torch.empty((Bb, w.Hq, w.d_v), dtype=torch.float32, device="cuda")
+
+    def pad(t, fill=0):
+        p = torch.full((Bb,) + tuple(t.shape[1:]), fill, dtype=t.dtype, device="cuda")
+        p[:w.B] = t
+        return p
+    rng = np.random.default_rng(99)
+    try:
+        for s in range(S):
+            k, v, slots, lens = _step_rows(w, kind, s)
+            if s == S - 1:
+                q_bits = w.q  # full contexts: the oracle's case
+            else:
+                q_bits = (rng.standard_normal(w.q.shape).astype(np.float32)
+                          .view(np.uint32) >> 16).astype(np.uint16)
+            q = bits_to_device(torch, q_bits)
+            k_d, v_d = bits_to_device(torch, k), bits_to_device(torch, v)
+            slots_d = torch.from_numpy(slots).cuda()
+            lens_d = torch.from_numpy(lens).cuda()
+            got = step(q, k_d, v_d, slots_d, bt, lens_d).clone()
+            # eager work and a synchronisation between replays
+            junk = torch.randn(1 << 16, device="cuda").sum()
+            torch.cuda.synchronize()
+            pkv.kv_append(kp_e, vp_e, pad(k_d), None if v_d is None else pad(v_d),
+                          pad(slots_d, -1), kv_dtype=w.kv_dtype)
+            if kind == "mla":
+                pkv.paged_decode_attn_mla(out_e, pad(q), kp_e, bt_pad, pad(lens_d), w.scale, Cb,
+                                          d_v=w.d_v)
+            else:
+                pkv.paged_decode_attn(out_e, pad(q), kp_e, vp_e, bt_pad, pad(lens_d), w.scale, Cb,
+                                      kv_dtype=w.kv_dtype, k_scale=ks, v_scale=vs)
+            torch.cuda.synchronize()
+            g, e = got.cpu().numpy(), out_e[:w.B].cpu().numpy()
+            assert np.isfinite(junk.item())
+            assert np.array_equal(g.view(np.uint32), e.view(np.uint32)), \
+                f"step {s}: replay differs from eager (max {np.abs(g - e).max():.3e})"
+            assert torch.equal(kp_g, kp_e), f"step {s}: K pool differs"
+            if vp_g is not None:
+                assert torch.equal(vp_g, vp_e), f"step {s}: V pool differs"
+        # every poisoned row is restored, and the last step matches the oracle
+        kg = kp_g.cpu().numpy()
+        assert np.array_equal(kg.view(w.k_pool.dtype), w.k_pool)
+        if vp_g is not None:
+            assert np.array_equal(vp_g.cpu().numpy().view(w.v_pool.dtype), w.v_pool)
+        assert_close(g, oracle_decode(w), w.kv_dtype, f"graph {kind} last step vs oracle")
+    finally:
+        step.close()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name,B,lens", [
+    ("tiny", 3, ("uniform", 40, 300)),
+    ("gqa70b", 5, ("uniform", 30, 700)),
+])
+def test_graph_gqa_steps_match_eager(name, B, lens):
+    w = make_workload(name, seed=31, B=B, lens=lens)
+    _run(w, "gqa")
+
+
+@pytest.mark.gpu
+def test_graph_mla_steps_match_eager():
+    w = make_workload("mla", seed=32, B=3, lens=("uniform", 70, 500))
+    _run(w, "mla")
+
+
+@pytest.mark.gpu
+def test_graph_begin_rejects_default_stream():
+    torch = torch_cuda()
+    import paged_kv_cache_288_amd as pkv
+    with torch.cuda.stream(torch.cuda.default_stream()):
+        with pytest.raises(pkv.PkvError):
+            pkv.graph_begin()
