@@ -152,6 +152,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--flush", action="store_true",
                     help="write 512 MiB of scratch before every step (outside the call's events)")
+    ap.add_argument("--append-fp8", action="store_true",
+                    help="FP8 workloads: append the new rows as bf16 through the quantizing append")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step's append and attention call as captured graphs")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -211,11 +213,23 @@ def main():
                                   kv_dtype=w.kv_dtype, k_scale=ks, v_scale=vs,
                                   partition_size=ps, workspace=ws)
 
+    append_fp8 = args.append_fp8 and w.kv_dtype == "fp8"
+    if append_fp8:
+        # the new rows as bf16 values (their stored codes decoded), quantized again on append
+        nk16 = (nk.view(torch.float8_e4m3fn).float() * ks[None, :, None]).to(torch.bfloat16)
+        nv16 = (nv.view(torch.float8_e4m3fn).float() * vs[None, :, None]).to(torch.bfloat16)
+
+    def append(kp, vp):
+        if append_fp8:
+            pkv.kv_append_fp8(kp, vp, nk16, nv16, ks, vs, slots)
+        else:
+            pkv.kv_append(kp, vp, nk, nv, slots, kv_dtype=w.kv_dtype)
+
     def step(i, ev=None):
         kp, vp = kps[i % args.layers], vps[i % args.layers]
         if flush_buf is not None:
             flush_buf.fill_(1)
-        pkv.kv_append(kp, vp, nk, nv, slots, kv_dtype=w.kv_dtype)
+        append(kp, vp)
         if ev is not None:
             ev[0].record()
         attend(kp, vp)
@@ -231,7 +245,7 @@ def main():
         with torch.cuda.stream(side):
             pkv.graph_begin()
             for i in range(args.layers):
-                pkv.kv_append(kps[i], vps[i], nk, nv, slots, kv_dtype=w.kv_dtype)
+                append(kps[i], vps[i])
                 attend(kps[i], vps[i])
             graph = pkv.graph_end()
         torch.cuda.current_stream().wait_stream(side)
@@ -317,6 +331,7 @@ def main():
             if w.kind != "mla" else ps,
             "kv_bytes_per_step": kvb, "flush_between_steps": bool(args.flush),
             "cache_copies_rotated": args.layers, "graph_replay": bool(args.graph),
+            "quantizing_append": bool(append_fp8),
         },
         "decode_tokens_per_s": round(w.B / (ms_per_step * 1e-3), 1),
         "hbm_peak_frac_step": round(kvb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

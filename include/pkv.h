@@ -190,6 +190,50 @@ pkv_status pkv_paged_decode_attn_mla(float* out, const void* q, const void* kv_p
                                      float scale, int32_t partition_size, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
+/*
+ * pkv_kv_append_fp8 — quantizing append ("PD 分离下的 KV Cache", "优化三：KV 传输优化": KV
+ * kept as FP8): token i's bf16 rows k_new/v_new [T][Hkv][d] are written as FP8 E4M3 (OCP
+ * e4m3fn) codes into slot_mapping[i] of the FP8 pools [num_blocks][Hkv][block_size][d],
+ * with the pools' per-KV-head scales k_scale/v_scale [Hkv] (fp32, device):
+ * code = the E4M3 value nearest to the fp32 quotient x / scale[h] (IEEE division), ties
+ * to the even code; magnitudes >= 448 and infinities saturate to +-448, NaN stays NaN.
+ * The decode call then reads code * scale[h].  v_pool and v_new may both be NULL (K only).
+ * Slots < 0 or outside the pool are skipped.  d must be a multiple of 16; pools and new
+ * rows 16-byte aligned, scales 4-byte aligned.  Errors as pkv_kv_append.
+ */
+pkv_status pkv_kv_append_fp8(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                             const float* k_scale, const float* v_scale,
+                             const int64_t* slot_mapping, int32_t T, int32_t num_blocks,
+                             int32_t Hkv, int32_t d, int32_t block_size, void* stream);
+
+/*
+ * pkv_kv_copy_blocks — copy-on-write support ("深入LLM推理：从KV Cache到PD分离的Serving全景
+ * 解析", "PagedAttention与Cache管理": physical blocks shared between requests): for i < n,
+ * physical block dst_blocks[i] of each pool becomes a copy of block src_blocks[i] (every
+ * KV head and row).  src_blocks/dst_blocks are device int32 arrays [n]; pairs with an id
+ * outside [0, num_blocks) are skipped; a block must not be both a source and a
+ * destination of one call.  Pools [num_blocks][Hkv][block_size][d] of kv_dtype (an MLA
+ * latent pool: Hkv = 1, v_pool NULL).  Errors: PKV_ERR_SHAPE, PKV_ERR_DTYPE, PKV_ERR_NULL,
+ * PKV_ERR_ALIGN (pools 16-byte aligned, rows a multiple of 16 bytes), PKV_ERR_HIP.
+ */
+pkv_status pkv_kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* src_blocks,
+                              const int32_t* dst_blocks, int32_t n, int32_t num_blocks,
+                              int32_t Hkv, int32_t d, int32_t block_size, int32_t kv_dtype,
+                              void* stream);
+
+/*
+ * pkv_block_hashes — host function, the prefix-cache key chain ("PD 分离下的 KV Cache",
+ * "优化一：Prefix Cache（前缀缓存）"): hash_i = H(hash_{i-1}, tokens of block i) for each of
+ * the n_tokens / block_size full blocks of `tokens` (host int32 array), hash_{-1} =
+ * `parent` (0 for a sequence start, or the hash of the block before, to continue a
+ * chain).  H is 64-bit FNV-1a over hash_{i-1} as 8 little-endian bytes followed by the
+ * block's tokens as little-endian int32.  Writes the hashes to `hashes` (host, room for
+ * n_tokens / block_size values) and returns their number; PKV_ERR_NULL / PKV_ERR_SHAPE on
+ * bad arguments.  No GPU work.
+ */
+int32_t pkv_block_hashes(const int32_t* tokens, int32_t n_tokens, int32_t block_size,
+                         uint64_t parent, uint64_t* hashes);
+
 /* ---- Graph capture of a decode step ("GPU推理深度拆解：KV Cache视角", "算子优化要点":
  * replaying a captured step removes the per-kernel launch overhead, at the price of static
  * shapes and addresses, so steps are padded to the nearest bucket).

@@ -14,7 +14,8 @@ __all__ = [
     "PKV_BF16", "PKV_FP8_E4M3", "PkvError", "library_path", "load_library",
     "abi_version", "kv_append", "decode_partition_size", "decode_workspace_bytes",
     "paged_decode_attn", "mla_workspace_bytes", "paged_decode_attn_mla", "Graph",
-    "graph_begin", "graph_end", "graph_launch", "graph_destroy",
+    "graph_begin", "graph_end", "graph_launch", "graph_destroy", "kv_append_fp8",
+    "kv_copy_blocks", "block_hashes",
 ]
 
 PKV_BF16 = 1
@@ -46,6 +47,11 @@ _SIGNATURES = [
     ("pkv_paged_decode_attn_mla", _c_int32, [_p, _p, _p, _p, _p, _c_int32, _c_int32, _c_int32,
                                              _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
                                              ctypes.c_float, _c_int32, _p, _c_size, _p]),
+    ("pkv_kv_append_fp8", _c_int32, [_p, _p, _p, _p, _p, _p, _p, _c_int32, _c_int32, _c_int32,
+                                     _c_int32, _c_int32, _p]),
+    ("pkv_kv_copy_blocks", _c_int32, [_p, _p, _p, _p, _c_int32, _c_int32, _c_int32, _c_int32,
+                                      _c_int32, _c_int32, _p]),
+    ("pkv_block_hashes", _c_int32, [_p, _c_int32, _c_int32, ctypes.c_uint64, _p]),
     ("pkv_graph_begin", _c_int32, [_p]),
     ("pkv_graph_end", _c_int32, [_p, ctypes.POINTER(ctypes.c_void_p)]),
     ("pkv_graph_launch", _c_int32, [_p, _p]),
@@ -186,6 +192,47 @@ def paged_decode_attn_mla(out, q, kv_pool, block_table, context_lens, scale, max
         partition_size, _ptr(workspace), wsize, _stream(q.device))
     _check("pkv_paged_decode_attn_mla", st)
     return out
+
+
+def kv_append_fp8(k_pool, v_pool, k_new, v_new, k_scale, v_scale, slot_mapping):
+    """Quantizing append (pkv_kv_append_fp8): bf16 rows k_new/v_new [T, Hkv, d] stored as
+    FP8 E4M3 codes of x / scale[h] into the uint8 pools [num_blocks, Hkv, block_size, d];
+    k_scale/v_scale [Hkv] fp32.  v_pool/v_new/v_scale may be None (K only)."""
+    num_blocks, Hkv, bs, d = k_pool.shape
+    T = slot_mapping.shape[0]
+    st = load_library().pkv_kv_append_fp8(
+        _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new), _ptr(k_scale), _ptr(v_scale),
+        _ptr(slot_mapping), T, num_blocks, Hkv, d, bs, _stream(k_pool.device))
+    _check("pkv_kv_append_fp8", st)
+
+
+def kv_copy_blocks(k_pool, v_pool, src_blocks, dst_blocks, kv_dtype="bf16"):
+    """Copy-on-write support (pkv_kv_copy_blocks): block dst[i] <- block src[i] in each pool.
+    Pools [num_blocks, Hkv, block_size, d] (an MLA latent pool [num_blocks, block_size,
+    d] with v_pool None); src/dst int32 device tensors [n]."""
+    if k_pool.dim() == 3:
+        num_blocks, bs, d = k_pool.shape
+        Hkv = 1
+    else:
+        num_blocks, Hkv, bs, d = k_pool.shape
+    st = load_library().pkv_kv_copy_blocks(
+        _ptr(k_pool), _ptr(v_pool), _ptr(src_blocks), _ptr(dst_blocks), src_blocks.shape[0],
+        num_blocks, Hkv, d, bs, _dtype_code(kv_dtype), _stream(k_pool.device))
+    _check("pkv_kv_copy_blocks", st)
+
+
+def block_hashes(tokens, block_size, parent=0):
+    """Prefix-cache keys of the full blocks of `tokens` (pkv_block_hashes, host): a numpy
+    uint64 array, hash_i = H(hash_{i-1}, tokens of block i), hash_{-1} = parent."""
+    import numpy as np
+    toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+    out = np.zeros(max(len(toks) // block_size, 0) if block_size > 0 else 0, dtype=np.uint64)
+    n = load_library().pkv_block_hashes(
+        toks.ctypes.data_as(ctypes.c_void_p), len(toks), block_size, int(parent) % (1 << 64),
+        out.ctypes.data_as(ctypes.c_void_p))
+    if n < 0:
+        _check("pkv_block_hashes", n)
+    return out[:n]
 
 
 class Graph:

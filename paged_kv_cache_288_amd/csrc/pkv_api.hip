@@ -340,6 +340,64 @@ pkv_status pkv_paged_decode_attn_mla(float* out, const void* q, const void* kv_p
                                                 max_blocks_per_seq * block_size, s));
 }
 
+pkv_status pkv_kv_append_fp8(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                             const float* k_scale, const float* v_scale,
+                             const int64_t* slot_mapping, int32_t T, int32_t num_blocks,
+                             int32_t Hkv, int32_t d, int32_t block_size, void* stream) {
+  if (T < 0 || num_blocks <= 0 || Hkv <= 0 || d <= 0 || block_size <= 0) return PKV_ERR_SHAPE;
+  if (T == 0) return PKV_OK;
+  if (!k_pool || !k_new || !k_scale || !slot_mapping) return PKV_ERR_NULL;
+  if ((v_pool == nullptr) != (v_new == nullptr) || (v_pool && !v_scale)) return PKV_ERR_NULL;
+  if (d % 16) return PKV_ERR_UNSUPPORTED;
+  if (!aligned16(k_pool) || !aligned16(k_new) || !aligned4(k_scale) ||
+      (v_pool && (!aligned16(v_pool) || !aligned16(v_new) || !aligned4(v_scale))) ||
+      ((uintptr_t)slot_mapping % 8))
+    return PKV_ERR_ALIGN;
+  pkv::AppendFp8Args a{(uint8_t*)k_pool, (uint8_t*)v_pool, (const uint16_t*)k_new,
+                       (const uint16_t*)v_new, k_scale, v_scale, slot_mapping, T,
+                       num_blocks, Hkv, block_size, d};
+  return hip_status(pkv::launch_kv_append_fp8(a, (hipStream_t)stream));
+}
+
+pkv_status pkv_kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* src_blocks,
+                              const int32_t* dst_blocks, int32_t n, int32_t num_blocks,
+                              int32_t Hkv, int32_t d, int32_t block_size, int32_t kv_dtype,
+                              void* stream) {
+  if (n < 0 || num_blocks <= 0 || Hkv <= 0 || d <= 0 || block_size <= 0) return PKV_ERR_SHAPE;
+  const int es = elem_bytes(kv_dtype);
+  if (!es) return PKV_ERR_DTYPE;
+  if (n == 0) return PKV_OK;
+  if (!k_pool || !src_blocks || !dst_blocks) return PKV_ERR_NULL;
+  if (((long long)d * es) % 16) return PKV_ERR_UNSUPPORTED;
+  if (!aligned16(k_pool) || (v_pool && !aligned16(v_pool)) || !aligned4(src_blocks) ||
+      !aligned4(dst_blocks))
+    return PKV_ERR_ALIGN;
+  pkv::CopyBlocksArgs a{(uint8_t*)k_pool, (uint8_t*)v_pool, src_blocks, dst_blocks, n,
+                        num_blocks, (int64_t)Hkv * block_size * d * es};
+  return hip_status(pkv::launch_kv_copy_blocks(a, (hipStream_t)stream));
+}
+
+int32_t pkv_block_hashes(const int32_t* tokens, int32_t n_tokens, int32_t block_size,
+                         uint64_t parent, uint64_t* hashes) {
+  if (n_tokens < 0 || block_size <= 0) return PKV_ERR_SHAPE;
+  const int32_t nb = n_tokens / block_size;
+  if (nb == 0) return 0;
+  if (!tokens || !hashes) return PKV_ERR_NULL;
+  uint64_t h = parent;
+  for (int32_t i = 0; i < nb; ++i) {
+    uint64_t x = 0xCBF29CE484222325ull;  // FNV-1a 64 offset basis
+    auto mix = [&x](uint8_t byte) { x = (x ^ byte) * 0x100000001B3ull; };
+    for (int k = 0; k < 8; ++k) mix((uint8_t)(h >> (8 * k)));
+    for (int32_t t = 0; t < block_size; ++t) {
+      const uint32_t v = (uint32_t)tokens[(size_t)i * block_size + t];
+      for (int k = 0; k < 4; ++k) mix((uint8_t)(v >> (8 * k)));
+    }
+    h = x;
+    hashes[i] = h;
+  }
+  return nb;
+}
+
 struct pkv_graph {
   hipGraph_t graph;
   hipGraphExec_t exec;

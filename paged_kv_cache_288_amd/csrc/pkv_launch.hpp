@@ -19,6 +19,28 @@ struct AppendArgs {
 };
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
 
+struct AppendFp8Args {
+  uint8_t* k_pool;  // [num_blocks][Hkv][block_size][d] E4M3 codes
+  uint8_t* v_pool;  // may be null (K only)
+  const uint16_t* k_new;  // [T][Hkv][d] bf16
+  const uint16_t* v_new;
+  const float* k_scale;  // [Hkv]
+  const float* v_scale;
+  const int64_t* slots;
+  int32_t T, num_blocks, Hkv, block_size, d;
+};
+hipError_t launch_kv_append_fp8(const AppendFp8Args& a, hipStream_t s);
+
+struct CopyBlocksArgs {
+  uint8_t* k_pool;
+  uint8_t* v_pool;  // may be null
+  const int32_t* src;
+  const int32_t* dst;
+  int32_t n, num_blocks;
+  int64_t block_bytes;  // bytes of one physical block of one pool (multiple of 16)
+};
+hipError_t launch_kv_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
+
 struct DecodeArgs {
   float* out;
   const uint16_t* q;

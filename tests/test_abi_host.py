@@ -236,3 +236,25 @@ def test_graph_buckets():
     assert bucket_context(8192, 16) == 8192 and bucket_context(8133, 64) == 8192
     with pytest.raises(ValueError):
         bucket_batch(0)
+
+
+def test_quantizing_append_and_block_copy_reject_bad_arguments(lib):
+    f = lib.pkv_kv_append_fp8
+    #          k_pool v_pool k_new v_new ks  vs  slots T  nb  H  d   bs  stream
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4, 2, 64, 16, None) == pkv.PKV_OK
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1, 4, 2, 64, 16, None) == pkv.PKV_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 3, 4, 2, 64, 16, None) == pkv.PKV_ERR_NULL
+    assert f(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 3, 4, 2, 64, 16, None) == pkv.PKV_ERR_NULL
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 3, 4, 2, 64, 16, None) == pkv.PKV_ERR_NULL
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 4, 2, 40, 16, None) == \
+        pkv.PKV_ERR_UNSUPPORTED
+    assert f(MIS, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 4, 2, 64, 16, None) == pkv.PKV_ERR_ALIGN
+    g = lib.pkv_kv_copy_blocks
+    #          k_pool v_pool src dst n nb H d bs dtype stream
+    assert g(FAKE, FAKE, FAKE, FAKE, 0, 4, 2, 64, 16, pkv.PKV_BF16, None) == pkv.PKV_OK
+    assert g(FAKE, FAKE, FAKE, FAKE, 2, 4, 2, 64, 16, 9, None) == pkv.PKV_ERR_DTYPE
+    assert g(FAKE, FAKE, None, FAKE, 2, 4, 2, 64, 16, pkv.PKV_BF16, None) == pkv.PKV_ERR_NULL
+    assert g(FAKE, FAKE, FAKE, FAKE, -1, 4, 2, 64, 16, pkv.PKV_BF16, None) == pkv.PKV_ERR_SHAPE
+    assert g(FAKE, MIS, FAKE, FAKE, 2, 4, 2, 64, 16, pkv.PKV_BF16, None) == pkv.PKV_ERR_ALIGN
+    assert g(FAKE, FAKE, FAKE, FAKE, 2, 4, 2, 4, 16, pkv.PKV_FP8_E4M3, None) == \
+        pkv.PKV_ERR_UNSUPPORTED
