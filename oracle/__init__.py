@@ -17,6 +17,7 @@ from .paged_attention import (  # noqa: F401
     decode_kv_bits,
     gather_sequence,
     paged_decode_attention,
+    multi_token_decode_attention,
     mla_decode_attention,
     kv_append,
     partition_partials,

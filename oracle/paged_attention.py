@@ -173,6 +173,24 @@ def mla_decode_attention(q, kv_pool, block_table, context_lens, scale, d_v):
     return paged_decode_attention(q, kv, kv[..., :d_v], block_table, context_lens, scale)
 
 
+def multi_token_decode_attention(q, k_pool, v_pool, block_table, context_lens, scale):
+    """Decode step with q_len query tokens per sequence (speculative verify).
+
+    [Serving] "投机解码：打破每步一token的假设": the large model checks the K drafted tokens
+    in one pass.  The new tokens' K/V are already in the cache and counted by
+    context_lens; causally, query token j of sequence b sees its first
+    context_lens[b] - q_len + 1 + j tokens (none: output 0).  q [B, q_len, Hq, d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, q_len = q.shape[:2]
+    lens = np.asarray(context_lens, dtype=np.int64)
+    out = np.zeros(q.shape[:3] + (np.asarray(v_pool).shape[-1],), dtype=np.float64)
+    for j in range(q_len):
+        lens_j = np.maximum(lens - (q_len - 1 - j), 0)
+        out[:, j] = paged_decode_attention(q[:, j], k_pool, v_pool, block_table, lens_j, scale)
+    return out
+
+
 # --------------------------------------------------------------------------
 # Append (the write half of a decode step)
 # --------------------------------------------------------------------------

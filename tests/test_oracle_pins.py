@@ -438,3 +438,37 @@ def test_unmutated_namespace_passes_every_pin():
     ns2 = _namespace(paged_decode_attention=_attn())
     for pin in PINS:
         pin(ns2)
+
+
+def test_multi_token_decode_is_causal_attention_over_the_new_tokens():
+    """Pinned against dense attention with an explicit causal mask over the gathered
+    sequence (the new tokens are its last q_len positions), q_len = 1 against the
+    single-token oracle, and a token whose context is empty against 0."""
+    rng = np.random.default_rng(21)
+    B, q_len, Hq, Hkv, d, bs = 3, 4, 4, 2, 8, 4
+    lens = np.array([9, 4, 2])
+    nb = 8
+    k_pool = rng.standard_normal((nb, Hkv, bs, d))
+    v_pool = rng.standard_normal((nb, Hkv, bs, d))
+    table = np.array([[3, 0, 6], [5, 1, 7], [2, 4, 7]])
+    q = rng.standard_normal((B, q_len, Hq, d))
+    got = REAL.multi_token_decode_attention(q, k_pool, v_pool, table, lens, 0.3)
+    G = Hq // Hkv
+    for b in range(B):
+        L = int(lens[b])
+        K = np.concatenate([k_pool[table[b, i]] for i in range(3)], axis=1)[:, :L]   # [Hkv, L, d]
+        V = np.concatenate([v_pool[table[b, i]] for i in range(3)], axis=1)[:, :L]
+        for h in range(Hq):
+            S = q[b, :, h] @ K[h // G].T * 0.3                      # [q_len, L]
+            pos = np.arange(L)[None, :]
+            row = (L - q_len + np.arange(q_len))[:, None]            # position of each new token
+            S = np.where(pos <= row, S, -np.inf)
+            for j in range(q_len):
+                if not np.isfinite(S[j]).any():
+                    assert np.all(got[b, j, h] == 0)
+                    continue
+                p = np.exp(S[j] - S[j].max())
+                assert np.allclose(got[b, j, h], p @ V[h // G] / p.sum(), rtol=1e-12, atol=1e-12)
+    one = REAL.multi_token_decode_attention(q[:, :1], k_pool, v_pool, table, lens, 0.3)
+    assert np.array_equal(one[:, 0], REAL.paged_decode_attention(q[:, 0], k_pool, v_pool,
+                                                                    table, lens, 0.3))
