@@ -39,6 +39,8 @@ KERNEL_SOURCES = {
             "paged_kv_cache_288_amd/csrc/gqa_tile.hpp", "paged_kv_cache_288_amd/csrc/pkv_device.hpp"],
     "mla": ["paged_kv_cache_288_amd/csrc/mla_stream.hip", "paged_kv_cache_288_amd/csrc/gqa_stream.hip",
             "paged_kv_cache_288_amd/csrc/gqa_tile.hpp", "paged_kv_cache_288_amd/csrc/pkv_device.hpp"],
+    "multi": ["paged_kv_cache_288_amd/csrc/gqa_multi.hip", "paged_kv_cache_288_amd/csrc/gqa_tile.hpp",
+              "paged_kv_cache_288_amd/csrc/pkv_device.hpp"],
 }
 
 
@@ -86,7 +88,17 @@ def traffic_for(workload_name, kind):
     return e.get("bytes_per_call")
 
 
+def kernel_family(w):
+    """Kernel sources a workload runs on: the latent kernels, the multi-token kernel, or the
+    single-token GQA kernels."""
+    if w.kind == "mla":
+        return "mla"
+    return "multi" if w.q_len > 1 else "gqa"
+
+
 def kernel_label(w, pkv, ps):
+    if w.q_len > 1:
+        return "pkv_paged_decode_attn_multi call (gqa_multi_kernel + multi_merge_kernel)"
     if w.kind == "mla":
         if ps == 0 and w.Hq % 64 == 0 and w.Hq <= 128:
             return "pkv_paged_decode_attn_mla call, balanced mode (mla_split_kernel + stream_merge_kernel<512>)"
@@ -116,7 +128,11 @@ def cpu_baseline(w, target_s=15.0):
         t0 = time.perf_counter()
         q = oracle.bf16_bits_to_f64(w.q[b:b + 1])
         table = np.arange(n)[None, :]
-        if w.kind == "mla":
+        if w.q_len > 1:
+            K = oracle.decode_kv_bits(w.k_pool[ids], w.kv_dtype, w.k_scale)
+            V = oracle.decode_kv_bits(w.v_pool[ids], w.kv_dtype, w.v_scale)
+            oracle.multi_token_decode_attention(q, K, V, table, w.context_lens[b:b + 1], w.scale)
+        elif w.kind == "mla":
             kv = oracle.bf16_bits_to_f64(w.k_pool[ids])
             oracle.mla_decode_attention(q, kv, table, w.context_lens[b:b + 1], w.scale, w.d_v)
         else:
@@ -135,8 +151,9 @@ def cpu_baseline(w, target_s=15.0):
         "cores": 1,
         "kind": "oracle",
         "sample": f"first {done} of {w.B} sequences ({tokens} cached tokens, all {w.Hq} "
-                  f"query heads), gather + fp64 attention, {t_total:.1f} s",
-        "decode_tokens_per_s": round(done / t_total, 4),
+                  f"query heads x {w.q_len} query tokens), gather + fp64 attention, "
+                  f"{t_total:.1f} s",
+        "decode_tokens_per_s": round(done * w.q_len / t_total, 4),
     }
 
 
@@ -194,9 +211,13 @@ def main():
     bt, cl = put(w.block_table), put(w.context_lens)
     ks, vs = put(w.k_scale), put(w.v_scale)
     nk, nv, slots = put(w.new_k), put(w.new_v), put(w.slot_mapping)
-    out = torch.empty((w.B, w.Hq, w.d_v), dtype=torch.float32, device=dev)
+    multi = w.q_len > 1
+    out = torch.empty((w.B, w.q_len, w.Hq, w.d_v) if multi else (w.B, w.Hq, w.d_v),
+                      dtype=torch.float32, device=dev)
     ps = w.partition_size if args.partition is None else args.partition
-    if w.kind == "mla":
+    if multi:
+        nbytes = pkv.multi_workspace_bytes(w.B, w.q_len, w.Hq, w.Hkv, w.d, w.max_context_len)
+    elif w.kind == "mla":
         nbytes = pkv.mla_workspace_bytes(w.B, w.Hq, w.d_v, w.max_context_len, ps)
     else:
         nbytes = pkv.decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, w.max_context_len, ps)
@@ -205,7 +226,10 @@ def main():
     torch.cuda.synchronize()
 
     def attend(kp, vp):
-        if w.kind == "mla":
+        if multi:
+            pkv.paged_decode_attn_multi(out, q, kp, vp, bt, cl, w.scale, w.max_context_len,
+                                        workspace=ws)
+        elif w.kind == "mla":
             pkv.paged_decode_attn_mla(out, q, kp, bt, cl, w.scale, w.max_context_len, d_v=w.d_v,
                                       partition_size=ps, workspace=ws)
         else:
@@ -309,6 +333,16 @@ def main():
             "hbm_achieved_GBs": round(achieved, 2),
             "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
         }
+    elif multi:
+        # q_len * G query rows share each K/V row: scores and p.V on the matrix cores, still
+        # below the ridge point, so the call is priced against HBM; the MFMA share beside it
+        flops = float(w.context_lens.astype(np.int64).sum()) * w.Hq * w.q_len * 2 * (w.d + w.d_v)
+        tflops = flops / (call_avg * 1e-3) / 1e12
+        roofline.update({
+            "algorithmic_flops_per_call": flops,
+            "mfma_achieved_TFLOPs": round(tflops, 2),
+            "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        })
     result = {
         "metric": METRIC,
         "value": round(kvb / (ms_per_step * 1e-3) / 1e9, 2),
@@ -331,13 +365,13 @@ def main():
             if w.kind != "mla" else ps,
             "kv_bytes_per_step": kvb, "flush_between_steps": bool(args.flush),
             "cache_copies_rotated": args.layers, "graph_replay": bool(args.graph),
-            "quantizing_append": bool(append_fp8),
+            "quantizing_append": bool(append_fp8), "query_tokens_per_sequence": w.q_len,
         },
-        "decode_tokens_per_s": round(w.B / (ms_per_step * 1e-3), 1),
+        "decode_tokens_per_s": round(w.B * w.q_len / (ms_per_step * 1e-3), 1),
         "hbm_peak_frac_step": round(kvb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {
             **roofline,
-            "traffic": traffic_for(w.name, w.kind),
+            "traffic": traffic_for(w.name, kernel_family(w)),
             "kernel": kernel_label(w, pkv, ps),
             "call_ms_avg": round(call_avg, 5),
             "call_ms_median": round(float(np.median(call_ms)), 5),

@@ -191,6 +191,42 @@ pkv_status pkv_paged_decode_attn_mla(float* out, const void* q, const void* kv_p
                                      size_t workspace_bytes, void* stream);
 
 /*
+ * pkv_multi_workspace_bytes — workspace bytes for pkv_paged_decode_attn_multi with these
+ * arguments (0 for an unsupported combination).
+ */
+size_t pkv_multi_workspace_bytes(int32_t B, int32_t q_len, int32_t Hq, int32_t Hkv, int32_t d,
+                                 int32_t max_context_len);
+
+/*
+ * pkv_paged_decode_attn_multi — decode step with q_len query tokens per sequence, the
+ * verify pass of speculative decoding.
+ *
+ * Cites: "深入LLM推理…" section "投机解码：打破每步一token的假设" (the target model checks
+ * the drafted tokens in one forward pass; nearly free while decode is memory-bound) and
+ * section "KV Cache：Transformer的循环状态" (softmax attention, GQA grouping).  The q_len new
+ * tokens' K/V rows are already in the cache (appended with pkv_kv_append) and counted by
+ * context_lens; the new tokens are causal among themselves:
+ *
+ *     L_j = context_lens[b] - q_len + 1 + j     (tokens that query token j sees)
+ *     out[b][j][h] = sum_{t < L_j} softmax_t(scale * dot(q[b][j][h], K[h / G][t])) V[h / G][t]
+ *
+ * (out = 0 where L_j <= 0).
+ *   out      [B][q_len][Hq][d] float32;  q [B][q_len][Hq][d] bfloat16
+ *   k_pool, v_pool, block_table, context_lens, max_context_len, workspace: as for
+ *   pkv_paged_decode_attn (the workspace size from pkv_multi_workspace_bytes).
+ * Supported: bf16 K/V, d in {64, 128}, block_size a multiple of 16, (Hq / Hkv) * q_len <=
+ * 64, B <= 4096.  Precision: scores on the bf16 MFMA, weights and V in fp16 on the fp16
+ * MFMA (fp32 accumulate), so |v| < 65504 as for the latent call.
+ */
+pkv_status pkv_paged_decode_attn_multi(float* out, const void* q, const void* k_pool,
+                                       const void* v_pool, const int32_t* block_table,
+                                       const int32_t* context_lens, int32_t B, int32_t q_len,
+                                       int32_t Hq, int32_t Hkv, int32_t d, int32_t block_size,
+                                       int32_t num_blocks, int32_t max_blocks_per_seq,
+                                       int32_t max_context_len, float scale, int32_t kv_dtype,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pkv_kv_append_fp8 — quantizing append ("PD 分离下的 KV Cache", "优化三：KV 传输优化": KV
  * kept as FP8): token i's bf16 rows k_new/v_new [T][Hkv][d] are written as FP8 E4M3 (OCP
  * e4m3fn) codes into slot_mapping[i] of the FP8 pools [num_blocks][Hkv][block_size][d],

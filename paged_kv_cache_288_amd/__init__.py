@@ -15,7 +15,7 @@ __all__ = [
     "abi_version", "kv_append", "decode_partition_size", "decode_workspace_bytes",
     "paged_decode_attn", "mla_workspace_bytes", "paged_decode_attn_mla", "Graph",
     "graph_begin", "graph_end", "graph_launch", "graph_destroy", "kv_append_fp8",
-    "kv_copy_blocks", "block_hashes",
+    "kv_copy_blocks", "block_hashes", "multi_workspace_bytes", "paged_decode_attn_multi",
 ]
 
 PKV_BF16 = 1
@@ -47,6 +47,12 @@ _SIGNATURES = [
     ("pkv_paged_decode_attn_mla", _c_int32, [_p, _p, _p, _p, _p, _c_int32, _c_int32, _c_int32,
                                              _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
                                              ctypes.c_float, _c_int32, _p, _c_size, _p]),
+    ("pkv_multi_workspace_bytes", _c_size, [_c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+                                            _c_int32]),
+    ("pkv_paged_decode_attn_multi", _c_int32, [_p, _p, _p, _p, _p, _p, _c_int32, _c_int32,
+                                               _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+                                               _c_int32, _c_int32, ctypes.c_float, _c_int32, _p,
+                                               _c_size, _p]),
     ("pkv_kv_append_fp8", _c_int32, [_p, _p, _p, _p, _p, _p, _p, _c_int32, _c_int32, _c_int32,
                                      _c_int32, _c_int32, _p]),
     ("pkv_kv_copy_blocks", _c_int32, [_p, _p, _p, _p, _c_int32, _c_int32, _c_int32, _c_int32,
@@ -191,6 +197,31 @@ def paged_decode_attn_mla(out, q, kv_pool, block_table, context_lens, scale, max
         d_v, bs, num_blocks, block_table.shape[1], max_context_len, float(scale),
         partition_size, _ptr(workspace), wsize, _stream(q.device))
     _check("pkv_paged_decode_attn_mla", st)
+    return out
+
+
+def multi_workspace_bytes(B, q_len, Hq, Hkv, d, max_context_len):
+    return load_library().pkv_multi_workspace_bytes(B, q_len, Hq, Hkv, d, max_context_len)
+
+
+def paged_decode_attn_multi(out, q, k_pool, v_pool, block_table, context_lens, scale,
+                            max_context_len, kv_dtype="bf16", workspace=None):
+    """out[B, q_len, Hq, d] (fp32) = multi-token decode attention, causal among each
+    sequence's q_len new tokens (pkv_paged_decode_attn_multi).
+
+    q [B, q_len, Hq, d] bf16; pools [num_blocks, Hkv, block_size, d]; context_lens count
+    the new tokens, whose K/V are already in the pools.
+    """
+    B, q_len, Hq, d = q.shape
+    num_blocks, Hkv, bs, _ = k_pool.shape
+    lib = load_library()
+    nbytes = lib.pkv_multi_workspace_bytes(B, q_len, Hq, Hkv, d, max_context_len)
+    workspace, wsize = _workspace(nbytes, q.device, workspace)
+    st = lib.pkv_paged_decode_attn_multi(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(context_lens),
+        B, q_len, Hq, Hkv, d, bs, num_blocks, block_table.shape[1], max_context_len,
+        float(scale), _dtype_code(kv_dtype), _ptr(workspace), wsize, _stream(q.device))
+    _check("pkv_paged_decode_attn_multi", st)
     return out
 
 

@@ -1,0 +1,473 @@
+// Multi-token paged decode attention (the verify step of speculative decoding) on gfx950.
+//
+// "深入LLM推理：从KV Cache到PD分离的Serving全景解析", section "投机解码：打破每步一token的假设":
+// the target model checks several drafted tokens in one pass, which is nearly free because
+// the step is bound by reading memory.  Here each sequence brings q_len new query tokens
+// whose K/V rows are already in the cache (counted by context_lens); query token j of a
+// sequence of length L sees its first L - q_len + 1 + j tokens (causal among the new ones):
+//     out[b][j][h] = softmax_t<L-q_len+1+j (scale * q[b][j][h] . K_t) V_t.
+//
+// All q_len * G query rows of a (sequence, KV head) pair share every K/V tile, so per byte
+// read the step does q_len times the arithmetic of a single-token decode (32 flop/byte at
+// G = 8, q_len = 4): past what the VALU sustains at HBM speed, and a dense contraction, so
+// both products run on the MFMA:
+//  * scores S^T[16 tokens x 16 rows] = K Q^T on v_mfma_f32_16x16x32_bf16 (D / 32 steps), K
+//    as the A operand straight from the 16-byte loads (lane l: token l % 16, 8 dims of a
+//    32-dim step chosen by l / 16), Q^T as the B operand held in registers for a piece;
+//  * the result gives lane l four tokens (4 (l / 16) + i) of query row l % 16, which is
+//    exactly the B operand layout of v_mfma_f32_16x16x16_f16, so the probabilities feed
+//    O^T[16 dims x 16 rows] += V^T P^T without moving across lanes, and each lane's output
+//    values and online-softmax state belong to its own row (rescales stay lane-local);
+//  * V^T (A operand: lane l holds dim l % 16 of 4 tokens) comes from LDS: each wave writes
+//    its V tile there token-major and reads it back with ds_read_b64_tr_b16, which
+//    transposes 4x4 blocks of 16-bit values across lanes; 32-byte pieces are XOR-swizzled
+//    per row so that the eight rows one half-wave reads lie in eight different bank groups.
+// Probabilities and V run through the fp16 MFMA (fp32 accumulate), as in the single-token
+// kernels: p <= 2^8 after the lazy max, V widened from bf16 exactly for 2^-14 <= |v| <
+// 65504.
+//
+// Division of work is the balanced mode of gqa_stream.hip: the 16-token tiles of all
+// (KV head, sequence) segments laid end to end, cut into equal ranges, one per wave; each
+// range yields one (m, l, o) piece per segment it meets, and multi_merge_kernel combines
+// the pieces of each segment.
+#include "gqa_tile.hpp"
+
+namespace pkv {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+constexpr int kMultiSeqs = 4096;      // sequences whose tile counts fit the LDS prefix
+constexpr int kMultiChunkTiles = 128; // tiles per chunk: two per lane
+constexpr int kMW = 4;                // waves per workgroup
+
+template <int D>
+struct MLayout {
+  static constexpr int ROW = 2 * D;                        // bytes per K or V row (bf16)
+  static constexpr int KS = D / 32;                        // score MFMA steps
+  static constexpr int NT = D / 16;                        // p.V MFMA dim blocks
+  static constexpr int VL = kTile * ROW / (16 * kWave);    // 16-byte V loads per lane per tile
+  static constexpr int TILE = kTile * ROW;                 // bytes of one K or V tile
+};
+
+// LDS position of the 32-byte piece p of V row t is p ^ vswz(t): the rows a half-wave's
+// transposed read touches (4 per 16-lane group, two groups) fall in distinct bank groups.
+template <int D>
+__device__ __forceinline__ int vswz(int t) {
+  if constexpr (D == 128) return t & 7;
+  else return (t >> 1) & 3;
+}
+
+__device__ __forceinline__ f32x4_t mfma_qk(const bf16x8_t& k, const bf16x8_t& q, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, q, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_pv(const f16x4_t& v, const f16x4_t& p, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(v, p, c, 0, 0, 0);
+}
+
+// Max / sum over the 4 lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float max4(float x) {
+  float lo, hi, e, o;
+  halves_pair32(x, lo, hi);
+  x = fmaxf(lo, hi);
+  rows_pair16(x, e, o);
+  return fmaxf(e, o);
+}
+__device__ __forceinline__ float sum4(float x) {
+  float lo, hi, e, o;
+  halves_pair32(x, lo, hi);
+  x = lo + hi;
+  rows_pair16(x, e, o);
+  return e + o;
+}
+
+template <int D>
+struct MTile {
+  uint4 k[MLayout<D>::KS];
+  uint4 v[MLayout<D>::VL];
+};
+
+template <int D>
+__device__ __forceinline__ void mload_k(MTile<D>& R, rsrc_t src, uint32_t koff) {
+#pragma unroll
+  for (int ks = 0; ks < MLayout<D>::KS; ++ks) R.k[ks] = buf_load16(src, koff + 64 * ks);
+}
+template <int D>
+__device__ __forceinline__ void mload_v(MTile<D>& R, rsrc_t src, uint32_t lane) {
+#pragma unroll
+  for (int u = 0; u < MLayout<D>::VL; ++u) R.v[u] = buf_load16(src, 1024 * u + 16 * lane);
+}
+
+}  // namespace
+
+// Waves per SIMD the register budget is sized for: two, except for 64 rows of 128 dims
+// (q and accumulators alone take 192 registers), which get the whole register file.
+constexpr int multi_waves_per_simd(int D, int RT) { return D * RT > 256 ? 1 : 2; }
+
+// Per wave: state of RT row tiles (16 query rows each) of the current piece.
+template <int D, int RT>
+__global__ __launch_bounds__(kMW * kWave, multi_waves_per_simd(D, RT)) void gqa_multi_kernel(MultiArgs a) {
+  using Lo = MLayout<D>;
+  __shared__ int s_pre[kMultiSeqs + 1];
+  __shared__ int s_sum[kMW * kWave];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[kMW][Lo::TILE];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int i16 = lane & 15, gq = lane >> 4;
+  const int B = a.B, G = a.Hq / a.Hkv, R = G * a.q_len;
+  const int cap = a.max_blocks * a.block_size;
+
+  // ---- tiles per sequence and their exclusive prefix, scanned across the workgroup
+  auto ntiles = [&](int bi) {
+    int L = a.context_lens[bi];
+    L = L < 0 ? 0 : (L > cap ? cap : L);
+    return (L + kTile - 1) / kTile;
+  };
+  const int per = (B + kMW * kWave - 1) / (kMW * kWave);
+  int local = 0;
+  for (int i = 0; i < per; ++i)
+    if (tid * per + i < B) local += ntiles(tid * per + i);
+  s_sum[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < kMW * kWave; off <<= 1) {
+    const int v = tid >= off ? s_sum[tid - off] : 0;
+    __syncthreads();
+    s_sum[tid] += v;
+    __syncthreads();
+  }
+  int run = tid == 0 ? 0 : s_sum[tid - 1];
+  for (int i = 0; i < per; ++i) {
+    const int bi = tid * per + i;
+    if (bi < B) {
+      s_pre[bi] = run;
+      run += ntiles(bi);
+    }
+  }
+  if (tid == 0) s_pre[B] = s_sum[kMW * kWave - 1];
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int i = tid; i <= B; i += kMW * kWave) a.ws_prefix[i] = s_pre[i];
+    write_segment_ranges(a.ws_seg, s_pre, B, a.Hkv, a.chunks, tid, kMW * kWave);
+  }
+
+  // ---- this wave's chunk (each XCD gets a contiguous eighth of the chunks)
+  const int T_head = __builtin_amdgcn_readfirstlane(s_pre[B]);
+  const long long T = (long long)a.Hkv * T_head;
+  const int C = a.chunks;
+  const int ch = (blockIdx.x & 7) * (C / 8) + (blockIdx.x >> 3) * kMW + w;
+  const long long tb = T * ch / C, te = T * (ch + 1) / C;
+  const int ntl = (int)min(te - tb, (long long)kMultiChunkTiles);
+  if (ntl <= 0) return;
+
+  // ---- per tile: byte offset / 256, valid tokens | segment << 5; and the first tile's
+  // index inside its sequence
+  const int tiles_per_block = a.block_size / kTile;
+  const size_t head_bytes = (size_t)a.block_size * Lo::ROW;
+  const size_t block_bytes = head_bytes * a.Hkv;
+  uint32_t off_l[2] = {0, 0};
+  int info_l[2] = {0, 0};
+  int tt_l = 0;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = kWave * j + lane;
+    if (n < ntl) {
+      const long long t = tb + n;
+      const int gg = (int)(t / T_head);
+      const int rem = (int)(t - (long long)gg * T_head);
+      int lo = 0, hi = B - 1;  // last sequence whose first tile is <= rem
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_pre[mid] <= rem) lo = mid;
+        else hi = mid - 1;
+      }
+      const int tt = rem - s_pre[lo];
+      int L = a.context_lens[lo];
+      L = L < 0 ? 0 : (L > cap ? cap : L);
+      const int phys = a.block_table[(size_t)lo * a.max_blocks + tt / tiles_per_block];
+      const bool ok = (unsigned)phys < (unsigned)a.num_blocks;
+      const uint64_t off = (uint64_t)(ok ? phys : 0) * block_bytes + (uint64_t)gg * head_bytes +
+                           (uint64_t)(tt % tiles_per_block) * Lo::TILE;
+      off_l[j] = (uint32_t)(off >> 8);
+      info_l[j] = (ok ? min(kTile, L - tt * kTile) : 0) | ((gg * B + lo) << 5);
+      if (j == 0) tt_l = tt;
+    }
+  }
+  const int tt_first = __builtin_amdgcn_readlane(tt_l, 0);
+  auto pick = [](int j, int x0, int x1) { return j ? x1 : x0; };
+  // Source of chunk tile n, or an empty one (all loads return zeros) for n >= end.
+  auto tile_at = [&](int n, int end) -> TileSrc {
+    if (n >= end) return TileSrc{make_rsrc(a.k_pool, 0), make_rsrc(a.v_pool, 0)};
+    const int j = n >> 6, ln = n & (kWave - 1);
+    const uint64_t off =
+        (uint64_t)(uint32_t)__builtin_amdgcn_readlane(pick(j, (int)off_l[0], (int)off_l[1]), ln) << 8;
+    const int nv = __builtin_amdgcn_readlane(pick(j, info_l[0], info_l[1]), ln) & 31;
+    return TileSrc{make_rsrc(a.k_pool + off, nv * Lo::ROW), make_rsrc(a.v_pool + off, nv * Lo::ROW)};
+  };
+  auto tile_seg = [&](int n) {
+    return __builtin_amdgcn_readlane(pick(n >> 6, info_l[0], info_l[1]), n & (kWave - 1)) >> 5;
+  };
+  uint64_t starts[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = kWave * j + lane;
+    const int seg = info_l[j] >> 5;
+    int prev = __shfl_up(seg, 1);
+    if (lane == 0) prev = j ? __builtin_amdgcn_readlane(info_l[0], kWave - 1) >> 5 : -1;
+    starts[j] = __builtin_amdgcn_ballot_w64(n < ntl && seg != prev);
+  }
+  auto next_start = [&](int n) {  // first piece start after tile n (or ntl)
+    for (int j = (n + 1) >> 6; j < 2; ++j) {
+      const int lo = (n + 1) - kWave * j;
+      const uint64_t m = lo <= 0 ? starts[j] : (lo >= kWave ? 0 : starts[j] & (~0ull << lo));
+      if (m) return kWave * j + (int)__builtin_ctzll(m);
+    }
+    return ntl;
+  };
+
+  // ---- LDS addresses of this lane's V writes and transposed reads
+  uint8_t* sv = s_v[w];
+  const lds_char_t* lsv = (const lds_char_t*)((lds_void_t*)sv);
+  uint32_t vw_off[Lo::VL];
+#pragma unroll
+  for (int u = 0; u < Lo::VL; ++u) {
+    const int gb = 1024 * u + 16 * lane, t = gb / Lo::ROW, col = gb % Lo::ROW;
+    vw_off[u] = t * Lo::ROW + 32 * ((col >> 5) ^ vswz<D>(t)) + (col & 16);
+  }
+  const int tr_row = 4 * gq + (i16 >> 2);
+  const uint32_t tr_base = tr_row * Lo::ROW + 8 * (i16 & 3);
+  const int tr_swz = vswz<D>(tr_row);
+  const uint32_t koff = (uint32_t)(i16 * Lo::ROW + 16 * gq);
+  const float cscale = a.scale * kLog2e;
+
+  MTile<D> RA, RB;
+  for (int n0 = 0; n0 < ntl;) {
+    const int n1 = next_start(n0);
+    const int seg = tile_seg(n0), gg = seg / B, bb = seg - gg * B;
+    int L = a.context_lens[bb];
+    L = L < 0 ? 0 : (L > cap ? cap : L);
+    const int t_first = (n0 == 0 ? tt_first : 0) * kTile;  // sequence position of tile n0
+
+    // q rows of the piece as the B operand; row limits relative to tile n0's first token
+    bf16x8_t qf[RT][Lo::KS];
+    int lim[RT];
+    f32x4_t o[RT][Lo::NT];
+    float m[RT], l[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int n = 16 * rt + i16;
+      const int jq = n / G;
+      const bool real = n < R;
+      lim[rt] = real ? L - a.q_len + 1 + jq - t_first : -1;
+      const uint8_t* qrow =
+          (const uint8_t*)(a.q + (((size_t)bb * a.q_len + (real ? jq : 0)) * a.Hq + (size_t)gg * G +
+                                  (real ? n - jq * G : 0)) * D);
+#pragma unroll
+      for (int ks = 0; ks < Lo::KS; ++ks) {
+        uint4 x = real ? *(const uint4*)(qrow + 64 * ks + 16 * gq) : uint4{0, 0, 0, 0};
+        qf[rt][ks] = __builtin_bit_cast(bf16x8_t, x);
+      }
+#pragma unroll
+      for (int nt = 0; nt < Lo::NT; ++nt) o[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      m[rt] = kNegInf;
+      l[rt] = 0.f;
+    }
+
+    // One tile of the piece (held in X): scores, online softmax, V through LDS, p.V; X is
+    // refilled with tile n_next (an empty tile past the piece's end).  pos0 = first token of
+    // the tile relative to tile n0.
+    auto step = [&](MTile<D>& X, int pos0, int n_next, int end) {
+      f32x4_t s[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        s[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < Lo::KS; ++ks)
+          s[rt] = mfma_qk(__builtin_bit_cast(bf16x8_t, X.k[ks]), qf[rt][ks], s[rt]);
+      }
+      sched_fence();
+      const TileSrc nx = tile_at(n_next, end);
+      mload_k<D>(X, nx.k, koff);
+      sched_fence();
+      // scores of tokens pos0 + 4 gq + i for this lane's row; masked past the row's limit
+      float mt[RT];
+      bool up = false;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        float x = kNegInf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = (pos0 + 4 * gq + i < lim[rt]) ? s[rt][i] * cscale : kNegInf;
+          s[rt][i] = v;
+          x = fmaxf(x, v);
+        }
+        mt[rt] = max4(x);
+        up |= mt[rt] > m[rt] + kRescaleSlack;
+      }
+      if (wave_any(up)) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const float m_new = fmaxf(m[rt], mt[rt]);
+          const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m[rt] - m_new);
+          l[rt] *= alpha;
+          m[rt] = m_new;
+#pragma unroll
+          for (int nt = 0; nt < Lo::NT; ++nt) o[rt][nt] *= alpha;
+        }
+      }
+      f16x4_t p[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const float mu = (m[rt] == kNegInf) ? 0.f : m[rt];
+        const uint32_t p01 = pack_f16(fast_exp2(s[rt][0] - mu), fast_exp2(s[rt][1] - mu));
+        const uint32_t p23 = pack_f16(fast_exp2(s[rt][2] - mu), fast_exp2(s[rt][3] - mu));
+        l[rt] = dot2h(p01, kOnesF16x2, l[rt]);
+        l[rt] = dot2h(p23, kOnesF16x2, l[rt]);
+        p[rt] = __builtin_bit_cast(f16x4_t, uint2{p01, p23});
+      }
+      // V tile -> LDS (token-major, swizzled), then refill X.v with the next tile
+#pragma unroll
+      for (int u = 0; u < Lo::VL; ++u) *(uint4*)(sv + vw_off[u]) = X.v[u];
+      sched_fence();
+      mload_v<D>(X, nx.v, lane);
+      sched_fence();
+#pragma unroll
+      for (int nt = 0; nt < Lo::NT; ++nt) {
+        const uint2 raw = __builtin_bit_cast(
+            uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                       (lds_s16x4_t*)(lsv + tr_base + 32 * (nt ^ tr_swz))));
+        const f16x4_t vf = __builtin_bit_cast(
+            f16x4_t, uint2{pack_f16(bf16_lo(raw.x), bf16_hi(raw.x)),
+                           pack_f16(bf16_lo(raw.y), bf16_hi(raw.y))});
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) o[rt][nt] = mfma_pv(vf, p[rt], o[rt][nt]);
+      }
+    };
+
+    {
+      const TileSrc A = tile_at(n0, n1), Bt = tile_at(n0 + 1, n1);
+      mload_k<D>(RA, A.k, koff);
+      sched_fence();
+      mload_v<D>(RA, A.v, lane);
+      sched_fence();
+      mload_k<D>(RB, Bt.k, koff);
+      sched_fence();
+      mload_v<D>(RB, Bt.v, lane);
+      sched_fence();
+    }
+    int n = n0;
+    for (; n + 1 < n1; n += 2) {
+      step(RA, kTile * (n - n0), n + 2, n1);
+      step(RB, kTile * (n + 1 - n0), n + 3, n1);
+    }
+    if (n < n1) step(RA, kTile * (n - n0), n + 2, n1);
+
+    // ---- the piece: rows n < R of slot ch + seg
+    const size_t slot = (size_t)ch + seg;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int nrow = 16 * rt + i16;
+      const float lt = sum4(l[rt]);
+      if (nrow < R) {
+        float* orow = a.ws_o + (slot * R + nrow) * D + 4 * gq;
+#pragma unroll
+        for (int nt = 0; nt < Lo::NT; ++nt)
+          *(float4*)(orow + 16 * nt) = make_float4(o[rt][nt][0], o[rt][nt][1], o[rt][nt][2], o[rt][nt][3]);
+        if (gq == 0) {
+          a.ws_m[slot * R + nrow] = m[rt];
+          a.ws_l[slot * R + nrow] = lt;
+        }
+      }
+    }
+    n0 = n1;
+  }
+}
+
+// out[b][j][hq] = merge of the pieces of segment (g = hq / G, b), row j * G + hq % G.
+// One wave per output row, kMergeWaves per workgroup.
+constexpr int kMultiMergeWaves = 4;
+template <int D>
+__global__ __launch_bounds__(kMultiMergeWaves * kWave) void multi_merge_kernel(MultiArgs a) {
+  constexpr int PER = D / kWave;
+  const int G = a.Hq / a.Hkv, R = G * a.q_len;
+  const int idx = blockIdx.x * kMultiMergeWaves + (int)(threadIdx.x / kWave);
+  if (idx >= a.B * a.q_len * a.Hq) return;
+  const int b = idx / (a.q_len * a.Hq), rem = idx - b * (a.q_len * a.Hq);
+  const int jq = rem / a.Hq, hq = rem - jq * a.Hq, g = hq / G, row = jq * G + (hq - g * G);
+  const int lane = threadIdx.x & (kWave - 1);
+  float* out = a.out + (size_t)idx * D;
+  const int c0 = a.ws_seg[2 * (g * a.B + b)], np = a.ws_seg[2 * (g * a.B + b) + 1];
+  const int T_head = a.ws_prefix[a.B];
+  if (np == 0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) out[lane + kWave * i] = 0.f;
+    return;
+  }
+  const long long T = (long long)a.Hkv * T_head;
+  const size_t slot0 = (size_t)c0 + (size_t)g * a.B + b;  // slot of piece i: slot0 + i
+  // with fewer tiles than chunks some chunks are empty and wrote nothing
+  const bool all_live = T >= a.chunks;
+  auto live = [&](int i) {
+    if (all_live) return true;
+    const long long cc = c0 + i;
+    return T * cc / a.chunks != T * (cc + 1) / a.chunks;
+  };
+  float M = kNegInf;
+  for (int p0 = 0; p0 < np; p0 += kWave)
+    if (p0 + lane < np && live(p0 + lane)) M = fmaxf(M, a.ws_m[(slot0 + p0 + lane) * R + row]);
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) M = fmaxf(M, __shfl_xor(M, s));
+  RowAcc<D> acc;
+  rows_clear(acc);
+  float den = 0.f;
+  for (int p0 = 0; p0 < np; p0 += kWave) {
+    float f = 0.f, lp = 0.f;
+    if (p0 + lane < np && live(p0 + lane)) {
+      const size_t si = (slot0 + p0 + lane) * R + row;
+      const float mp = a.ws_m[si];
+      lp = a.ws_l[si];
+      f = (mp == kNegInf) ? 0.f : fast_exp2(mp - M);
+    }
+    float fl = f * lp;
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) fl += __shfl_xor(fl, s);
+    den += fl;
+    rows_accumulate<D>(acc, a.ws_o + ((slot0 + p0) * R + row) * D, (size_t)R * D, f,
+                       min(kWave, np - p0), lane);
+  }
+  rows_store<D>(acc, out, den > 0.f ? 1.f / den : 0.f, lane);
+}
+
+template <int D, int RT>
+static hipError_t launch_multi_one(const MultiArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((gqa_multi_kernel<D, RT>), dim3(a.chunks / kMW), dim3(kMW * kWave), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)(((long long)a.B * a.q_len * a.Hq + kMultiMergeWaves - 1) / kMultiMergeWaves));
+  hipLaunchKernelGGL(multi_merge_kernel<D>, grid, dim3(kMultiMergeWaves * kWave), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_multi_d(const MultiArgs& a, hipStream_t s) {
+  const int R = a.Hq / a.Hkv * a.q_len;
+  if (R <= 16) return launch_multi_one<D, 1>(a, s);
+  if (R <= 32) return launch_multi_one<D, 2>(a, s);
+  if (R <= 64) return launch_multi_one<D, 4>(a, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gqa_multi(const MultiArgs& a, hipStream_t s) {
+  if (a.B > kMultiSeqs || a.chunks % 32 || a.block_size % kTile) return hipErrorInvalidValue;
+  if (a.d == 128) return launch_multi_d<128>(a, s);
+  if (a.d == 64) return launch_multi_d<64>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

@@ -138,6 +138,21 @@ pkv_status hip_status(hipError_t e) {
   return PKV_ERR_HIP;
 }
 
+// Multi-token workspace: the balanced layout with R = q_len * Hq / Hkv rows per piece slot.
+size_t multi_ws_bytes(int32_t B, int32_t q_len, int32_t Hq, int32_t Hkv, int32_t d,
+                      int32_t chunks) {
+  const size_t rows = ((size_t)chunks + (size_t)Hkv * B) * (size_t)(Hq / Hkv) * q_len;
+  return 2 * round256(rows * sizeof(float)) + round256(rows * d * sizeof(float)) +
+         round256(((size_t)B + 1) * sizeof(int32_t)) +
+         round256((size_t)Hkv * B * 2 * sizeof(int32_t));
+}
+
+bool multi_shape_ok(int32_t B, int32_t q_len, int32_t Hq, int32_t Hkv, int32_t d,
+                    int32_t max_context_len) {
+  return B >= 0 && q_len > 0 && Hq > 0 && Hkv > 0 && Hq % Hkv == 0 && d > 0 &&
+         max_context_len >= 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -338,6 +353,54 @@ pkv_status pkv_paged_decode_attn_mla(float* out, const void* q, const void* kv_p
   return hip_status(pkv::launch_partition_merge(ws_m, ws_l, ws_o, context_lens, out, B, Hq, d_v,
                                                 ps, P, ctx,
                                                 max_blocks_per_seq * block_size, s));
+}
+
+size_t pkv_multi_workspace_bytes(int32_t B, int32_t q_len, int32_t Hq, int32_t Hkv, int32_t d,
+                                 int32_t max_context_len) {
+  if (!multi_shape_ok(B, q_len, Hq, Hkv, d, max_context_len)) return 0;
+  if ((long long)(Hq / Hkv) * q_len > 64 || (long long)Hkv * B >= (1LL << 26)) return 0;
+  const int32_t chunks = stream_chunks(B, Hkv, max_context_len);
+  return chunks < 0 ? 0 : multi_ws_bytes(B, q_len, Hq, Hkv, d, chunks);
+}
+
+pkv_status pkv_paged_decode_attn_multi(float* out, const void* q, const void* k_pool,
+                                       const void* v_pool, const int32_t* block_table,
+                                       const int32_t* context_lens, int32_t B, int32_t q_len,
+                                       int32_t Hq, int32_t Hkv, int32_t d, int32_t block_size,
+                                       int32_t num_blocks, int32_t max_blocks_per_seq,
+                                       int32_t max_context_len, float scale, int32_t kv_dtype,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (!multi_shape_ok(B, q_len, Hq, Hkv, d, max_context_len) || block_size <= 0 ||
+      num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return PKV_ERR_SHAPE;
+  if (!elem_bytes(kv_dtype)) return PKV_ERR_DTYPE;
+  if (B == 0) return PKV_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_table || !context_lens) return PKV_ERR_NULL;
+  if (kv_dtype != PKV_BF16 || (d != 128 && d != 64) || block_size % 16 ||
+      (long long)(Hq / Hkv) * q_len > 64)
+    return PKV_ERR_UNSUPPORTED;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      !aligned4(block_table) || !aligned4(context_lens))
+    return PKV_ERR_ALIGN;
+  if (B > kMaxStreamSeqs || (long long)Hkv * B >= (1LL << 26)) return PKV_ERR_SHAPE;
+  const int32_t chunks = stream_chunks(B, Hkv, max_context_len);
+  if (chunks < 0) return PKV_ERR_SHAPE;
+  if (!workspace || workspace_bytes < multi_ws_bytes(B, q_len, Hq, Hkv, d, chunks))
+    return PKV_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+  const size_t rows = ((size_t)chunks + (size_t)Hkv * B) * (size_t)(Hq / Hkv) * q_len;
+  char* base = (char*)workspace;
+  float* ws_m = (float*)base;
+  float* ws_l = (float*)(base + round256(rows * sizeof(float)));
+  float* ws_o = (float*)(base + 2 * round256(rows * sizeof(float)));
+  int32_t* ws_p = (int32_t*)(base + 2 * round256(rows * sizeof(float)) +
+                             round256(rows * d * sizeof(float)));
+  int32_t* ws_s = (int32_t*)((char*)ws_p + round256(((size_t)B + 1) * sizeof(int32_t)));
+  pkv::MultiArgs a{out, (const uint16_t*)q, (const uint8_t*)k_pool, (const uint8_t*)v_pool,
+                   block_table, context_lens, ws_m, ws_l, ws_o, ws_p, ws_s,
+                   B, q_len, Hq, Hkv, d, block_size, num_blocks, max_blocks_per_seq,
+                   scale, chunks};
+  return hip_status(pkv::launch_gqa_multi(a, (hipStream_t)stream));
 }
 
 pkv_status pkv_kv_append_fp8(void* k_pool, void* v_pool, const void* k_new, const void* v_new,

@@ -100,4 +100,25 @@ hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t s);
 int mla_stream_heads_per_group(int Hq);
 hipError_t launch_mla_stream(const MlaArgs& a, hipStream_t s);
 
+// Multi-token decode (q_len query tokens per sequence, causal among them), balanced mode
+// only.  Row n of segment (g, b) is query token n / G, head g * G + n % G.
+struct MultiArgs {
+  float* out;           // [B][q_len][Hq][d]
+  const uint16_t* q;    // [B][q_len][Hq][d] bf16
+  const uint8_t* k_pool;
+  const uint8_t* v_pool;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  float* ws_m;  // [S][R], S = chunks + Hkv * B piece slots, R = q_len * Hq / Hkv rows
+  float* ws_l;  // [S][R]
+  float* ws_o;  // [S][R][d]
+  int32_t* ws_prefix;  // [B + 1]
+  int32_t* ws_seg;     // [Hkv * B][2]
+  int32_t B, q_len, Hq, Hkv, d, block_size, num_blocks, max_blocks;
+  float scale;
+  int32_t chunks;  // one per wave, a multiple of 32
+};
+// Decode kernel + merge kernel.
+hipError_t launch_gqa_multi(const MultiArgs& a, hipStream_t s);
+
 }  // namespace pkv

@@ -53,17 +53,18 @@ class Workload:
     kv_dtype: str                # "bf16" or "fp8"
     scale: float
     partition_size: int          # 0 = library default
-    q: np.ndarray                # uint16 [B, Hq, d]
+    q: np.ndarray                # uint16 [B, Hq, d] ([B, q_len, Hq, d] when q_len > 1)
     k_pool: np.ndarray           # [nb, Hkv, bs, d] (MLA: [nb, bs, d])
     v_pool: object               # [nb, Hkv, bs, d_v] or None for MLA
     k_scale: object              # float32 [Hkv] (FP8) or None
     v_scale: object
     block_table: np.ndarray      # int32 [B, max_blocks], -1 padded
     context_lens: np.ndarray     # int32 [B]
-    new_k: np.ndarray            # bits [B, Hkv, d]: the token at position L_b - 1
-    new_v: object                # bits [B, Hkv, d_v] or None (MLA)
-    slot_mapping: np.ndarray     # int64 [B]
+    new_k: np.ndarray            # bits [B * q_len, Hkv, d]: the tokens at L_b - q_len .. L_b - 1
+    new_v: object                # bits [B * q_len, Hkv, d_v] or None (MLA)
+    slot_mapping: np.ndarray     # int64 [B * q_len] (-1 for a position before the sequence)
     meta: dict = field(default_factory=dict)
+    q_len: int = 1               # new query tokens per sequence (multi-token decode)
 
     @property
     def num_blocks(self):
@@ -101,6 +102,11 @@ SPECS = {
         kind="mla", B=32, Hq=128, Hkv=1, d=576, d_v=512, bs=64, kv_dtype="bf16",
         scale=1.0 / math.sqrt(192), lens=("uniform", 2048, 8192), pool=("factor", 1.25),
         partition_size=0)),
+    # The 70B-shaped batch verifying 4 new tokens per sequence (speculative decoding:
+    # "深入LLM推理…", section "投机解码：打破每步一token的假设"); context lengths include them.
+    "gqa70b-verify4-b64-h64x8-d128-ctx1k-8k": (5, dict(
+        kind="gqa", B=64, Hq=64, Hkv=8, d=128, bs=16, kv_dtype="bf16", scale=1.0 / math.sqrt(128),
+        lens=("uniform", 1024, 8192), pool=("factor", 1.25), partition_size=0, q_len=4)),
 }
 
 # Short aliases used on command lines.
@@ -110,6 +116,7 @@ ALIASES = {
     "splitk": "gqa-splitk-b4-h64x8-d128-ctx32k",
     "fp8prefix": "gqa-fp8-prefix4k-b128-h32x8-d128",
     "mla": "mla-b32-h128-d576-ctx2k-8k",
+    "verify4": "gqa70b-verify4-b64-h64x8-d128-ctx1k-8k",
 }
 
 
@@ -142,9 +149,10 @@ def _lengths(rng, spec, B):
     raise ValueError(kind)
 
 
-def make_workload(name, seed=0, B=None, lens=None, pool=None, heads=None):
+def make_workload(name, seed=0, B=None, lens=None, pool=None, heads=None, q_len=None):
     """Build a workload by name (or alias); ``B``/``lens``/``pool``/``heads`` (a pair
-    Hq, Hkv) override the spec to make reduced-size variants of the same structure."""
+    Hq, Hkv)/``q_len`` override the spec to make reduced-size variants of the same
+    structure.  With q_len > 1, q holds q_len query tokens per sequence."""
     name = ALIASES.get(name, name)
     index, spec = SPECS[name]
     spec = dict(spec)
@@ -156,6 +164,9 @@ def make_workload(name, seed=0, B=None, lens=None, pool=None, heads=None):
         spec["pool"] = pool
     if heads is not None:
         spec["Hq"], spec["Hkv"] = heads
+    if q_len is not None:
+        spec["q_len"] = q_len
+    q_len = int(spec.get("q_len", 1))
     rng = np.random.default_rng([288, index, seed])
     kind = spec["kind"]
     B, Hq, Hkv, d, bs = spec["B"], spec["Hq"], spec["Hkv"], spec["d"], spec["bs"]
@@ -199,7 +210,8 @@ def make_workload(name, seed=0, B=None, lens=None, pool=None, heads=None):
         cursor += k
 
     # 4. q
-    q = to_bf16_bits(rng.standard_normal((B, Hq, d), dtype=np.float32))
+    qshape = (B, Hq, d) if q_len == 1 else (B, q_len, Hq, d)
+    q = to_bf16_bits(rng.standard_normal(qshape, dtype=np.float32))
 
     # 5.-7. K and V, sequence by sequence over written slots only
     heads = 1 if kind == "mla" else Hkv
@@ -262,18 +274,24 @@ def make_workload(name, seed=0, B=None, lens=None, pool=None, heads=None):
         if v_pool is not None:
             store(v_pool, ids, vb, v_scale)
 
-    # The decode step's own token: position L_b - 1 (already in the pool, so
-    # appending it again leaves the pool unchanged).
-    pos = lens - 1
-    phys = table[np.arange(B), pos // bs].astype(np.int64)
-    off = pos % bs
-    slot_mapping = (phys * bs + off).astype(np.int64)
+    # The decode step's own tokens: positions L_b - q_len .. L_b - 1 (already in the
+    # pool, so appending them again leaves the pool unchanged).
+    pos = (lens[:, None] - q_len + np.arange(q_len)[None, :]).reshape(-1)
+    seq = np.repeat(np.arange(B), q_len)
+    live = pos >= 0
+    posc = np.where(live, pos, 0)
+    phys = table[seq, posc // bs].astype(np.int64)
+    off = posc % bs
+    slot_mapping = np.where(live, phys * bs + off, -1).astype(np.int64)
     if kind == "mla":
         new_k = k_pool[phys, off][:, None, :].copy()
         new_v = None
     else:
         new_k = k_pool[phys, :, off, :].copy()
         new_v = v_pool[phys, :, off, :].copy()
+        if not live.all():
+            new_k[~live] = new_k.dtype.type(0)
+            new_v[~live] = new_v.dtype.type(0)
 
     return Workload(
         name=name, kind=kind, B=B, Hq=Hq, Hkv=Hkv, d=d, d_v=d_v, bs=bs,
@@ -282,5 +300,5 @@ def make_workload(name, seed=0, B=None, lens=None, pool=None, heads=None):
         q=q, k_pool=k_pool, v_pool=v_pool, k_scale=k_scale, v_scale=v_scale,
         block_table=table, context_lens=lens.astype(np.int32),
         new_k=new_k, new_v=new_v, slot_mapping=slot_mapping,
-        meta=dict(prefix_blocks=prefix_blocks, seed=seed),
+        meta=dict(prefix_blocks=prefix_blocks, seed=seed), q_len=q_len,
     )

@@ -258,3 +258,42 @@ def test_quantizing_append_and_block_copy_reject_bad_arguments(lib):
     assert g(FAKE, MIS, FAKE, FAKE, 2, 4, 2, 64, 16, pkv.PKV_BF16, None) == pkv.PKV_ERR_ALIGN
     assert g(FAKE, FAKE, FAKE, FAKE, 2, 4, 2, 4, 16, pkv.PKV_FP8_E4M3, None) == \
         pkv.PKV_ERR_UNSUPPORTED
+
+
+def test_multi_rejects_bad_arguments_before_launch(lib):
+    f = lib.pkv_paged_decode_attn_multi
+    # out q k v bt cl B q_len Hq Hkv d bs nb mb ctx scale dtype ws wsb stream
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 64, 8, 128, 16, 10, 4, 64, 0.1,
+            pkv.PKV_BF16, None, 0, None]
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a7=0) == -2              # q_len
+    assert call(a8=60) == -2             # Hq not a multiple of Hkv
+    assert call(a16=9) == -3
+    assert call(a6=0) == 0               # empty batch
+    assert call(a0=None) == -1
+    assert call(a7=9) == -4              # 72 rows per KV head
+    assert call(a16=pkv.PKV_FP8_E4M3) == -4
+    assert call(a10=96) == -4
+    assert call(a11=8) == -4
+    assert call(a1=MIS) == -5
+    assert call() == -6                  # needs a workspace
+    assert call(a17=FAKE, a18=64) == -6
+
+
+def test_multi_workspace_size(lib):
+    """Balanced layout with q_len * G rows per piece slot; 256 CUs assumed without a GPU."""
+    r256 = lambda x: (x + 255) // 256 * 256
+    for B, q_len, Hq, Hkv, d, ctx in [(64, 4, 64, 8, 128, 8192), (2, 8, 4, 1, 64, 256),
+                                      (1, 1, 8, 8, 128, 20000), (3, 16, 32, 8, 128, 900)]:
+        tmax = Hkv * B * -(-ctx // 16)
+        C = max(min(8 * 256, tmax), -(-tmax // 128))
+        C = max(32, -(-C // 32) * 32)
+        rows = (C + Hkv * B) * (Hq // Hkv) * q_len
+        want = 2 * r256(rows * 4) + r256(rows * d * 4) + r256((B + 1) * 4) + r256(Hkv * B * 8)
+        assert lib.pkv_multi_workspace_bytes(B, q_len, Hq, Hkv, d, ctx) == want
+    assert lib.pkv_multi_workspace_bytes(2, 9, 64, 8, 128, 100) == 0     # 72 rows
+    assert lib.pkv_multi_workspace_bytes(2, 0, 64, 8, 128, 100) == 0

@@ -77,3 +77,23 @@ def test_key_boost_scales_one_percent_of_keys():
     K = bf16_bits_to_f64(gather_sequence(w.k_pool, w.block_table[0], 1600, 16))
     norms = np.abs(K).mean(axis=2)                        # [Hkv, L]
     assert ((norms > 3.0).sum(axis=1) == 16).all()
+
+
+def test_multi_token_workload_structure():
+    """q_len > 1: q [B, q_len, Hq, d]; the step's tokens are the last q_len positions of
+    each sequence, their slots and rows read back from the pool (-1 before position 0)."""
+    w = make_workload("gqa70b", seed=3, B=5, lens=("fixed", [0, 2, 16, 17, 300]), q_len=4)
+    assert w.q.shape == (5, 4, 64, 128) and w.q_len == 4
+    assert w.slot_mapping.shape == (20,) and w.new_k.shape == (20, 8, 128)
+    for b, L in enumerate(w.context_lens):
+        for j in range(4):
+            pos, i = int(L) - 4 + j, 4 * b + j
+            if pos < 0:
+                assert w.slot_mapping[i] == -1
+                continue
+            phys = int(w.block_table[b, pos // 16])
+            assert w.slot_mapping[i] == phys * 16 + pos % 16
+            assert np.array_equal(w.new_k[i], w.k_pool[phys, :, pos % 16])
+            assert np.array_equal(w.new_v[i], w.v_pool[phys, :, pos % 16])
+    full = make_workload("verify4")
+    assert (full.B, full.q_len, full.Hq, full.Hkv, full.d) == (64, 4, 64, 8, 128)
