@@ -107,13 +107,18 @@ __device__ __forceinline__ void mload_v(MTile<D>& R, rsrc_t src, uint32_t lane) 
 
 }  // namespace
 
-// Waves per SIMD the register budget is sized for: two, except for 64 rows of 128 dims
-// (q and accumulators alone take 192 registers), which get the whole register file.
-constexpr int multi_waves_per_simd(int D, int RT) { return D * RT > 256 ? 1 : 2; }
+// Tiles in flight per wave (each a K and a V register buffer) and waves per SIMD: two
+// buffers at two waves per SIMD, except for 64 rows of 128 dims (q and accumulators alone
+// take 192 registers), which get the whole register file.
+constexpr int multi_buffers(int D, int RT) { return 2; }
+constexpr int multi_waves_per_simd(int D, int RT) {
+  return (D * RT > 256 || multi_buffers(D, RT) > 2) ? 1 : 2;
+}
 
 // Per wave: state of RT row tiles (16 query rows each) of the current piece.
 template <int D, int RT>
 __global__ __launch_bounds__(kMW * kWave, multi_waves_per_simd(D, RT)) void gqa_multi_kernel(MultiArgs a) {
+  constexpr int NB = multi_buffers(D, RT);
   using Lo = MLayout<D>;
   __shared__ int s_pre[kMultiSeqs + 1];
   __shared__ int s_sum[kMW * kWave];
@@ -246,7 +251,7 @@ __global__ __launch_bounds__(kMW * kWave, multi_waves_per_simd(D, RT)) void gqa_
   const uint32_t koff = (uint32_t)(i16 * Lo::ROW + 16 * gq);
   const float cscale = a.scale * kLog2e;
 
-  MTile<D> RA, RB;
+  MTile<D> Rb[NB];
   for (int n0 = 0; n0 < ntl;) {
     const int n1 = next_start(n0);
     const int seg = tile_seg(n0), gg = seg / B, bb = seg - gg * B;
@@ -350,23 +355,24 @@ __global__ __launch_bounds__(kMW * kWave, multi_waves_per_simd(D, RT)) void gqa_
       }
     };
 
-    {
-      const TileSrc A = tile_at(n0, n1), Bt = tile_at(n0 + 1, n1);
-      mload_k<D>(RA, A.k, koff);
+    // tile n lives in buffer (n - n0) % NB; loads are issued in tile order (the scheduling
+    // fences keep it), so the waits the compiler derives stay exact
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const TileSrc S = tile_at(n0 + b, n1);
+      mload_k<D>(Rb[b], S.k, koff);
       sched_fence();
-      mload_v<D>(RA, A.v, lane);
-      sched_fence();
-      mload_k<D>(RB, Bt.k, koff);
-      sched_fence();
-      mload_v<D>(RB, Bt.v, lane);
+      mload_v<D>(Rb[b], S.v, lane);
       sched_fence();
     }
     int n = n0;
-    for (; n + 1 < n1; n += 2) {
-      step(RA, kTile * (n - n0), n + 2, n1);
-      step(RB, kTile * (n + 1 - n0), n + 3, n1);
+    for (; n + NB - 1 < n1; n += NB) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) step(Rb[b], kTile * (n + b - n0), n + b + NB, n1);
     }
-    if (n < n1) step(RA, kTile * (n - n0), n + 2, n1);
+#pragma unroll
+    for (int b = 0; b < NB - 1; ++b)
+      if (n + b < n1) step(Rb[b], kTile * (n + b - n0), n + b + NB, n1);
 
     // ---- the piece: rows n < R of slot ch + seg
     const size_t slot = (size_t)ch + seg;
@@ -461,6 +467,12 @@ static hipError_t launch_multi_d(const MultiArgs& a, hipStream_t s) {
   if (R <= 32) return launch_multi_one<D, 2>(a, s);
   if (R <= 64) return launch_multi_one<D, 4>(a, s);
   return hipErrorInvalidValue;
+}
+
+int multi_waves_per_cu(int d, int rows) {
+  const int rt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+  if (d == 128) return kMW * multi_waves_per_simd(128, rt);
+  return kMW * multi_waves_per_simd(64, rt);
 }
 
 hipError_t launch_gqa_multi(const MultiArgs& a, hipStream_t s) {

@@ -84,13 +84,14 @@ int device_cus() {
   return cached[dev];
 }
 
-// Balanced mode: one chunk per wave, two 4-wave workgroups per CU, and enough chunks that
+// Balanced mode: one chunk per resident wave (two 4-wave workgroups per CU for the
+// single-token kernel), and enough chunks that
 // none holds more than kMaxChunkTiles tiles even if every context were max_context_len;
 // never more chunks than that bound on the tiles (rounded up to 32), so that a small
 // batch is not spread over thousands of empty chunks the merge would walk.
-int32_t stream_chunks(int32_t B, int32_t Hkv, int32_t max_ctx) {
+int32_t stream_chunks(int32_t B, int32_t Hkv, int32_t max_ctx, int waves_per_cu = 8) {
   const long long tmax = (long long)Hkv * B * ((max_ctx + 15) / 16);
-  long long c = 8LL * device_cus();
+  long long c = (long long)waves_per_cu * device_cus();
   if (tmax < c) c = tmax;
   const long long need = (tmax + kMaxChunkTiles - 1) / kMaxChunkTiles;
   if (need > c) c = need;
@@ -145,6 +146,12 @@ size_t multi_ws_bytes(int32_t B, int32_t q_len, int32_t Hq, int32_t Hkv, int32_t
   return 2 * round256(rows * sizeof(float)) + round256(rows * d * sizeof(float)) +
          round256(((size_t)B + 1) * sizeof(int32_t)) +
          round256((size_t)Hkv * B * 2 * sizeof(int32_t));
+}
+
+int32_t multi_chunks(int32_t B, int32_t q_len, int32_t Hq, int32_t Hkv, int32_t d,
+                     int32_t max_context_len) {
+  return stream_chunks(B, Hkv, max_context_len,
+                       pkv::multi_waves_per_cu(d, (Hq / Hkv) * q_len));
 }
 
 bool multi_shape_ok(int32_t B, int32_t q_len, int32_t Hq, int32_t Hkv, int32_t d,
@@ -359,7 +366,7 @@ size_t pkv_multi_workspace_bytes(int32_t B, int32_t q_len, int32_t Hq, int32_t H
                                  int32_t max_context_len) {
   if (!multi_shape_ok(B, q_len, Hq, Hkv, d, max_context_len)) return 0;
   if ((long long)(Hq / Hkv) * q_len > 64 || (long long)Hkv * B >= (1LL << 26)) return 0;
-  const int32_t chunks = stream_chunks(B, Hkv, max_context_len);
+  const int32_t chunks = multi_chunks(B, q_len, Hq, Hkv, d, max_context_len);
   return chunks < 0 ? 0 : multi_ws_bytes(B, q_len, Hq, Hkv, d, chunks);
 }
 
@@ -383,7 +390,7 @@ pkv_status pkv_paged_decode_attn_multi(float* out, const void* q, const void* k_
       !aligned4(block_table) || !aligned4(context_lens))
     return PKV_ERR_ALIGN;
   if (B > kMaxStreamSeqs || (long long)Hkv * B >= (1LL << 26)) return PKV_ERR_SHAPE;
-  const int32_t chunks = stream_chunks(B, Hkv, max_context_len);
+  const int32_t chunks = multi_chunks(B, q_len, Hq, Hkv, d, max_context_len);
   if (chunks < 0) return PKV_ERR_SHAPE;
   if (!workspace || workspace_bytes < multi_ws_bytes(B, q_len, Hq, Hkv, d, chunks))
     return PKV_ERR_WORKSPACE;

@@ -120,5 +120,7 @@ struct MultiArgs {
 };
 // Decode kernel + merge kernel.
 hipError_t launch_gqa_multi(const MultiArgs& a, hipStream_t s);
+// Resident waves per CU of the multi-token decode kernel for head dim d and q_len * G rows.
+int multi_waves_per_cu(int d, int rows);
 
 }  // namespace pkv

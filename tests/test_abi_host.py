@@ -290,7 +290,9 @@ def test_multi_workspace_size(lib):
     for B, q_len, Hq, Hkv, d, ctx in [(64, 4, 64, 8, 128, 8192), (2, 8, 4, 1, 64, 256),
                                       (1, 1, 8, 8, 128, 20000), (3, 16, 32, 8, 128, 900)]:
         tmax = Hkv * B * -(-ctx // 16)
-        C = max(min(8 * 256, tmax), -(-tmax // 128))
+        rows = (Hq // Hkv) * q_len
+        waves = 4 if d * -(-rows // 16) > 256 else 8      # resident waves per CU
+        C = max(min(waves * 256, tmax), -(-tmax // 128))
         C = max(32, -(-C // 32) * 32)
         rows = (C + Hkv * B) * (Hq // Hkv) * q_len
         want = 2 * r256(rows * 4) + r256(rows * d * 4) + r256((B + 1) * 4) + r256(Hkv * B * 8)
