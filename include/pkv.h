@@ -212,19 +212,70 @@ size_t pkv_multi_workspace_bytes(int32_t B, int32_t q_len, int32_t Hq, int32_t H
  *
  * (out = 0 where L_j <= 0).
  *   out      [B][q_len][Hq][d] float32;  q [B][q_len][Hq][d] bfloat16
- *   k_pool, v_pool, block_table, context_lens, max_context_len, workspace: as for
- *   pkv_paged_decode_attn (the workspace size from pkv_multi_workspace_bytes).
- * Supported: bf16 K/V, d in {64, 128}, block_size a multiple of 16, (Hq / Hkv) * q_len <=
- * 64, B <= 4096.  Precision: scores on the bf16 MFMA, weights and V in fp16 on the fp16
- * MFMA (fp32 accumulate), so |v| < 65504 as for the latent call.
+ *   k_pool, v_pool, k_scale, v_scale, kv_dtype, block_table, context_lens,
+ *   max_context_len, workspace: as for pkv_paged_decode_attn (the workspace size from
+ *   pkv_multi_workspace_bytes).
+ * Supported: bf16 or FP8 K/V, d in {64, 128}, block_size a multiple of 16,
+ * (Hq / Hkv) * q_len <= 64, B <= 4096.  Precision: scores on the bf16 MFMA (FP8 codes
+ * widened exactly to bf16), weights and V in fp16 on the fp16 MFMA (fp32 accumulate), so
+ * |v| < 65504 as for the latent call.
  */
 pkv_status pkv_paged_decode_attn_multi(float* out, const void* q, const void* k_pool,
-                                       const void* v_pool, const int32_t* block_table,
+                                       const void* v_pool, const float* k_scale,
+                                       const float* v_scale, const int32_t* block_table,
                                        const int32_t* context_lens, int32_t B, int32_t q_len,
                                        int32_t Hq, int32_t Hkv, int32_t d, int32_t block_size,
                                        int32_t num_blocks, int32_t max_blocks_per_seq,
                                        int32_t max_context_len, float scale, int32_t kv_dtype,
                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_cascade_workspace_bytes — workspace bytes for pkv_paged_decode_attn_cascade with
+ * these arguments (0 for an invalid combination).
+ */
+size_t pkv_cascade_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                                   int32_t prefix_len, int32_t max_tail_len);
+
+/*
+ * pkv_paged_decode_attn_cascade — decode step for a batch whose sequences all start with
+ * the same cached prefix.
+ *
+ * Cites: "深入LLM推理…" section "PagedAttention与Cache管理" (several sequences' block tables
+ * point at the same physical blocks of a common prefix) and "PD 分离下的 KV Cache" section
+ * "优化一：Prefix Cache（前缀缓存）" (requests sharing a system prompt reuse its KV).  The
+ * result is exactly that of pkv_paged_decode_attn with block_table[b] = prefix_blocks
+ * followed by tail_table[b] and context_lens[b] = prefix_len + tail_lens[b]:
+ *
+ *     out[b][h] = sum_t softmax_t(scale * dot(q[b][h], K_t)) V_t over the prefix's tokens
+ *                 and then sequence b's own tail tokens (KV head h / G).
+ *
+ * The prefix is read once per group of 64 / G sequences, with the whole group's query rows
+ * as one dense product on the matrix cores, instead of once per sequence; the tails run
+ * through the single-token kernel, and one merge combines both.
+ *   out            [B][Hq][d] float32;  q [B][Hq][d] bfloat16
+ *   k_pool, v_pool, k_scale, v_scale, kv_dtype, scale: as for pkv_paged_decode_attn
+ *   prefix_blocks  [prefix_len / block_size] int32 physical block ids (device); NULL
+ *                  allowed when prefix_len = 0.  prefix_len: a multiple of block_size
+ *                  (a partially filled shared block belongs to the tails).
+ *   tail_table     [B][max_tail_blocks] int32;  tail_lens [B] int32 in
+ *                  [0, max_tail_blocks * block_size] (clamped); max_tail_len >= every
+ *                  tail length (sizes the work split and the workspace).
+ *   workspace      >= pkv_cascade_workspace_bytes(...) device bytes, 16-byte aligned.
+ * A sequence with no token at all (prefix_len = 0 and an empty tail) gets out = 0.
+ * Supported: Hq / Hkv in {1, 2, 4, 8}, d = 128 (bf16 or FP8) or 64 (bf16), block_size a
+ * multiple of 16, B <= 4096.  Precision: tails as pkv_paged_decode_attn; the prefix as
+ * pkv_paged_decode_attn_multi (bf16 MFMA scores, fp16 MFMA p.V, FP8 codes widened
+ * exactly).
+ */
+pkv_status pkv_paged_decode_attn_cascade(float* out, const void* q, const void* k_pool,
+                                         const void* v_pool, const float* k_scale,
+                                         const float* v_scale, const int32_t* prefix_blocks,
+                                         int32_t prefix_len, const int32_t* tail_table,
+                                         const int32_t* tail_lens, int32_t B, int32_t Hq,
+                                         int32_t Hkv, int32_t d, int32_t block_size,
+                                         int32_t num_blocks, int32_t max_tail_blocks,
+                                         int32_t max_tail_len, float scale, int32_t kv_dtype,
+                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pkv_kv_append_fp8 — quantizing append ("PD 分离下的 KV Cache", "优化三：KV 传输优化": KV

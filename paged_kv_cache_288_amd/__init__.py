@@ -16,6 +16,7 @@ __all__ = [
     "paged_decode_attn", "mla_workspace_bytes", "paged_decode_attn_mla", "Graph",
     "graph_begin", "graph_end", "graph_launch", "graph_destroy", "kv_append_fp8",
     "kv_copy_blocks", "block_hashes", "multi_workspace_bytes", "paged_decode_attn_multi",
+    "cascade_workspace_bytes", "paged_decode_attn_cascade",
 ]
 
 PKV_BF16 = 1
@@ -49,10 +50,16 @@ _SIGNATURES = [
                                              ctypes.c_float, _c_int32, _p, _c_size, _p]),
     ("pkv_multi_workspace_bytes", _c_size, [_c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
                                             _c_int32]),
-    ("pkv_paged_decode_attn_multi", _c_int32, [_p, _p, _p, _p, _p, _p, _c_int32, _c_int32,
+    ("pkv_paged_decode_attn_multi", _c_int32, [_p, _p, _p, _p, _p, _p, _p, _p, _c_int32,
                                                _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
-                                               _c_int32, _c_int32, ctypes.c_float, _c_int32, _p,
-                                               _c_size, _p]),
+                                               _c_int32, _c_int32, _c_int32, ctypes.c_float,
+                                               _c_int32, _p, _c_size, _p]),
+    ("pkv_cascade_workspace_bytes", _c_size, [_c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+                                              _c_int32]),
+    ("pkv_paged_decode_attn_cascade", _c_int32, [_p, _p, _p, _p, _p, _p, _p, _c_int32, _p, _p,
+                                                 _c_int32, _c_int32, _c_int32, _c_int32,
+                                                 _c_int32, _c_int32, _c_int32, _c_int32,
+                                                 ctypes.c_float, _c_int32, _p, _c_size, _p]),
     ("pkv_kv_append_fp8", _c_int32, [_p, _p, _p, _p, _p, _p, _p, _c_int32, _c_int32, _c_int32,
                                      _c_int32, _c_int32, _p]),
     ("pkv_kv_copy_blocks", _c_int32, [_p, _p, _p, _p, _c_int32, _c_int32, _c_int32, _c_int32,
@@ -205,12 +212,13 @@ def multi_workspace_bytes(B, q_len, Hq, Hkv, d, max_context_len):
 
 
 def paged_decode_attn_multi(out, q, k_pool, v_pool, block_table, context_lens, scale,
-                            max_context_len, kv_dtype="bf16", workspace=None):
+                            max_context_len, kv_dtype="bf16", k_scale=None, v_scale=None,
+                            workspace=None):
     """out[B, q_len, Hq, d] (fp32) = multi-token decode attention, causal among each
     sequence's q_len new tokens (pkv_paged_decode_attn_multi).
 
     q [B, q_len, Hq, d] bf16; pools [num_blocks, Hkv, block_size, d]; context_lens count
-    the new tokens, whose K/V are already in the pools.
+    the new tokens, whose K/V are already in the pools; k_scale/v_scale [Hkv] for FP8.
     """
     B, q_len, Hq, d = q.shape
     num_blocks, Hkv, bs, _ = k_pool.shape
@@ -218,10 +226,35 @@ def paged_decode_attn_multi(out, q, k_pool, v_pool, block_table, context_lens, s
     nbytes = lib.pkv_multi_workspace_bytes(B, q_len, Hq, Hkv, d, max_context_len)
     workspace, wsize = _workspace(nbytes, q.device, workspace)
     st = lib.pkv_paged_decode_attn_multi(
-        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(context_lens),
-        B, q_len, Hq, Hkv, d, bs, num_blocks, block_table.shape[1], max_context_len,
-        float(scale), _dtype_code(kv_dtype), _ptr(workspace), wsize, _stream(q.device))
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_table), _ptr(context_lens), B, q_len, Hq, Hkv, d, bs, num_blocks,
+        block_table.shape[1], max_context_len, float(scale), _dtype_code(kv_dtype),
+        _ptr(workspace), wsize, _stream(q.device))
     _check("pkv_paged_decode_attn_multi", st)
+    return out
+
+
+def cascade_workspace_bytes(B, Hq, Hkv, d, prefix_len, max_tail_len):
+    return load_library().pkv_cascade_workspace_bytes(B, Hq, Hkv, d, prefix_len, max_tail_len)
+
+
+def paged_decode_attn_cascade(out, q, k_pool, v_pool, prefix_blocks, prefix_len, tail_table,
+                              tail_lens, scale, max_tail_len, kv_dtype="bf16", k_scale=None,
+                              v_scale=None, workspace=None):
+    """out[B, Hq, d] (fp32) = decode attention over a shared prefix (prefix_blocks
+    [prefix_len / block_size] int32) followed by each sequence's tail (tail_table
+    [B, max_tail_blocks] int32, tail_lens [B] int32) (pkv_paged_decode_attn_cascade)."""
+    B, Hq, d = q.shape
+    num_blocks, Hkv, bs, _ = k_pool.shape
+    lib = load_library()
+    nbytes = lib.pkv_cascade_workspace_bytes(B, Hq, Hkv, d, prefix_len, max_tail_len)
+    workspace, wsize = _workspace(nbytes, q.device, workspace)
+    st = lib.pkv_paged_decode_attn_cascade(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+        _ptr(prefix_blocks), prefix_len, _ptr(tail_table), _ptr(tail_lens), B, Hq, Hkv, d, bs,
+        num_blocks, tail_table.shape[1], max_tail_len, float(scale), _dtype_code(kv_dtype),
+        _ptr(workspace), wsize, _stream(q.device))
+    _check("pkv_paged_decode_attn_cascade", st)
     return out
 
 

@@ -48,13 +48,16 @@ constexpr int kMultiSeqs = 4096;      // sequences whose tile counts fit the LDS
 constexpr int kMultiChunkTiles = 128; // tiles per chunk: two per lane
 constexpr int kMW = 4;                // waves per workgroup
 
-template <int D>
+template <int D, bool FP8>
 struct MLayout {
-  static constexpr int ROW = 2 * D;                        // bytes per K or V row (bf16)
+  static constexpr int ROW = FP8 ? D : 2 * D;              // bytes per K or V row in HBM
+  static constexpr int LROW = 2 * D;                       // bytes per V row in LDS (16-bit)
   static constexpr int KS = D / 32;                        // score MFMA steps
+  static constexpr int KL = FP8 ? D / 64 : D / 32;         // 16-byte K loads per lane per tile
   static constexpr int NT = D / 16;                        // p.V MFMA dim blocks
   static constexpr int VL = kTile * ROW / (16 * kWave);    // 16-byte V loads per lane per tile
-  static constexpr int TILE = kTile * ROW;                 // bytes of one K or V tile
+  static constexpr int TILE = kTile * ROW;                 // bytes of one K or V tile in HBM
+  static constexpr int LTILE = kTile * LROW;               // bytes of one V tile in LDS
 };
 
 // LDS position of the 32-byte piece p of V row t is p ^ vswz(t): the rows a half-wave's
@@ -88,21 +91,46 @@ __device__ __forceinline__ float sum4(float x) {
   return e + o;
 }
 
-template <int D>
+template <int D, bool FP8>
 struct MTile {
-  uint4 k[MLayout<D>::KS];
-  uint4 v[MLayout<D>::VL];
+  uint4 k[MLayout<D, FP8>::KL];
+  uint4 v[MLayout<D, FP8>::VL];
 };
 
-template <int D>
-__device__ __forceinline__ void mload_k(MTile<D>& R, rsrc_t src, uint32_t koff) {
-#pragma unroll
-  for (int ks = 0; ks < MLayout<D>::KS; ++ks) R.k[ks] = buf_load16(src, koff + 64 * ks);
+// K pieces of lane l: token l % 16; the dims of MFMA step ks for lane group g = l / 16 are
+// 32 ks + 8 g .. + 7 (bf16: one 16-byte load per step) or D/4 g + 8 ks .. + 7 (FP8: the
+// group's D/4 contiguous bytes in D/64 loads).  q is read with the same map.
+template <int D, bool FP8>
+__device__ __forceinline__ uint32_t k_offset(int i16, int g, int j) {
+  using Lo = MLayout<D, FP8>;
+  return FP8 ? (uint32_t)(i16 * Lo::ROW + g * (D / 4) + 16 * j)
+             : (uint32_t)(i16 * Lo::ROW + 16 * g + 64 * j);
 }
-template <int D>
-__device__ __forceinline__ void mload_v(MTile<D>& R, rsrc_t src, uint32_t lane) {
+template <int D, bool FP8>
+__device__ __forceinline__ uint32_t q_offset(int g, int ks) {  // bytes into a bf16 q row
+  return FP8 ? (uint32_t)(g * (D / 2) + 16 * ks) : (uint32_t)(64 * ks + 16 * g);
+}
+template <int D, bool FP8>
+__device__ __forceinline__ void mload_k(MTile<D, FP8>& R, rsrc_t src, uint32_t koff) {
 #pragma unroll
-  for (int u = 0; u < MLayout<D>::VL; ++u) R.v[u] = buf_load16(src, 1024 * u + 16 * lane);
+  for (int j = 0; j < MLayout<D, FP8>::KL; ++j) R.k[j] = buf_load16(src, koff + (FP8 ? 16 : 64) * j);
+}
+template <int D, bool FP8>
+__device__ __forceinline__ void mload_v(MTile<D, FP8>& R, rsrc_t src, uint32_t lane) {
+#pragma unroll
+  for (int u = 0; u < MLayout<D, FP8>::VL; ++u) R.v[u] = buf_load16(src, 1024 * u + 16 * lane);
+}
+// A operand of score step ks: 8 bf16 K values (FP8 codes widened exactly).
+template <int D, bool FP8>
+__device__ __forceinline__ bf16x8_t k_frag(const MTile<D, FP8>& R, int ks) {
+  if constexpr (FP8) {
+    const uint4 x = R.k[ks >> 1];
+    const uint32_t w0 = (ks & 1) ? x.z : x.x, w1 = (ks & 1) ? x.w : x.y;
+    return __builtin_bit_cast(bf16x8_t, uint4{fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
+                                              fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1)});
+  } else {
+    return __builtin_bit_cast(bf16x8_t, R.k[ks]);
+  }
 }
 
 }  // namespace
@@ -116,25 +144,25 @@ constexpr int multi_waves_per_simd(int D, int RT) {
 }
 
 // Per wave: state of RT row tiles (16 query rows each) of the current piece.
-template <int D, int RT>
+template <int D, int RT, bool FP8>
 __global__ __launch_bounds__(kMW * kWave, multi_waves_per_simd(D, RT)) void gqa_multi_kernel(MultiArgs a) {
   constexpr int NB = multi_buffers(D, RT);
-  using Lo = MLayout<D>;
+  using Lo = MLayout<D, FP8>;
   __shared__ int s_pre[kMultiSeqs + 1];
   __shared__ int s_sum[kMW * kWave];
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[kMW][Lo::TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[kMW][Lo::LTILE];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int i16 = lane & 15, gq = lane >> 4;
   const int B = a.B, G = a.Hq / a.Hkv, R = G * a.q_len;
   const int cap = a.max_blocks * a.block_size;
+  auto seq_len = [&](int bi) {  // clamped to the table; one length for all in prefix mode
+    int L = a.fixed_len >= 0 ? a.fixed_len : a.context_lens[bi];
+    return L < 0 ? 0 : (L > cap ? cap : L);
+  };
 
   // ---- tiles per sequence and their exclusive prefix, scanned across the workgroup
-  auto ntiles = [&](int bi) {
-    int L = a.context_lens[bi];
-    L = L < 0 ? 0 : (L > cap ? cap : L);
-    return (L + kTile - 1) / kTile;
-  };
+  auto ntiles = [&](int bi) { return (seq_len(bi) + kTile - 1) / kTile; };
   const int per = (B + kMW * kWave - 1) / (kMW * kWave);
   int local = 0;
   for (int i = 0; i < per; ++i)
@@ -193,9 +221,8 @@ __global__ __launch_bounds__(kMW * kWave, multi_waves_per_simd(D, RT)) void gqa_
         else hi = mid - 1;
       }
       const int tt = rem - s_pre[lo];
-      int L = a.context_lens[lo];
-      L = L < 0 ? 0 : (L > cap ? cap : L);
-      const int phys = a.block_table[(size_t)lo * a.max_blocks + tt / tiles_per_block];
+      const int L = seq_len(lo);
+      const int phys = a.block_table[(size_t)lo * a.table_stride + tt / tiles_per_block];
       const bool ok = (unsigned)phys < (unsigned)a.num_blocks;
       const uint64_t off = (uint64_t)(ok ? phys : 0) * block_bytes + (uint64_t)gg * head_bytes +
                            (uint64_t)(tt % tiles_per_block) * Lo::TILE;
@@ -239,25 +266,27 @@ __global__ __launch_bounds__(kMW * kWave, multi_waves_per_simd(D, RT)) void gqa_
   // ---- LDS addresses of this lane's V writes and transposed reads
   uint8_t* sv = s_v[w];
   const lds_char_t* lsv = (const lds_char_t*)((lds_void_t*)sv);
+  // V load u of this lane holds 16 bytes at 1024 u + 16 lane of the tile: 8 bf16 (half a
+  // 32-byte LDS piece) or 16 FP8 codes (a whole piece once widened to fp16)
   uint32_t vw_off[Lo::VL];
 #pragma unroll
   for (int u = 0; u < Lo::VL; ++u) {
-    const int gb = 1024 * u + 16 * lane, t = gb / Lo::ROW, col = gb % Lo::ROW;
-    vw_off[u] = t * Lo::ROW + 32 * ((col >> 5) ^ vswz<D>(t)) + (col & 16);
+    const int gb = 1024 * u + 16 * lane, t = gb / Lo::ROW, e0 = (gb % Lo::ROW) / (FP8 ? 1 : 2);
+    vw_off[u] = t * Lo::LROW + 32 * ((e0 >> 4) ^ vswz<D>(t)) + 2 * (e0 & 15);
   }
   const int tr_row = 4 * gq + (i16 >> 2);
-  const uint32_t tr_base = tr_row * Lo::ROW + 8 * (i16 & 3);
+  const uint32_t tr_base = tr_row * Lo::LROW + 8 * (i16 & 3);
   const int tr_swz = vswz<D>(tr_row);
-  const uint32_t koff = (uint32_t)(i16 * Lo::ROW + 16 * gq);
-  const float cscale = a.scale * kLog2e;
+  const uint32_t koff = k_offset<D, FP8>(i16, gq, 0);
 
-  MTile<D> Rb[NB];
+  MTile<D, FP8> Rb[NB];
   for (int n0 = 0; n0 < ntl;) {
     const int n1 = next_start(n0);
     const int seg = tile_seg(n0), gg = seg / B, bb = seg - gg * B;
-    int L = a.context_lens[bb];
-    L = L < 0 ? 0 : (L > cap ? cap : L);
+    const int L = seq_len(bb);
     const int t_first = (n0 == 0 ? tt_first : 0) * kTile;  // sequence position of tile n0
+    const float cscale = a.scale * kLog2e * (FP8 ? a.k_scale[gg] : 1.f);
+    const float vs = FP8 ? a.v_scale[gg] : 1.f;
 
     // q rows of the piece as the B operand; row limits relative to tile n0's first token
     bf16x8_t qf[RT][Lo::KS];
@@ -268,14 +297,14 @@ __global__ __launch_bounds__(kMW * kWave, multi_waves_per_simd(D, RT)) void gqa_
     for (int rt = 0; rt < RT; ++rt) {
       const int n = 16 * rt + i16;
       const int jq = n / G;
-      const bool real = n < R;
-      lim[rt] = real ? L - a.q_len + 1 + jq - t_first : -1;
+      const bool real = n < R && bb * a.q_len + jq < a.q_rows;
+      lim[rt] = real ? L - (a.causal ? a.q_len - 1 - jq : 0) - t_first : -1;
       const uint8_t* qrow =
           (const uint8_t*)(a.q + (((size_t)bb * a.q_len + (real ? jq : 0)) * a.Hq + (size_t)gg * G +
                                   (real ? n - jq * G : 0)) * D);
 #pragma unroll
       for (int ks = 0; ks < Lo::KS; ++ks) {
-        uint4 x = real ? *(const uint4*)(qrow + 64 * ks + 16 * gq) : uint4{0, 0, 0, 0};
+        uint4 x = real ? *(const uint4*)(qrow + q_offset<D, FP8>(gq, ks)) : uint4{0, 0, 0, 0};
         qf[rt][ks] = __builtin_bit_cast(bf16x8_t, x);
       }
 #pragma unroll
@@ -287,18 +316,20 @@ __global__ __launch_bounds__(kMW * kWave, multi_waves_per_simd(D, RT)) void gqa_
     // One tile of the piece (held in X): scores, online softmax, V through LDS, p.V; X is
     // refilled with tile n_next (an empty tile past the piece's end).  pos0 = first token of
     // the tile relative to tile n0.
-    auto step = [&](MTile<D>& X, int pos0, int n_next, int end) {
+    auto step = [&](MTile<D, FP8>& X, int pos0, int n_next, int end) {
       f32x4_t s[RT];
+      bf16x8_t kf[Lo::KS];
+#pragma unroll
+      for (int ks = 0; ks < Lo::KS; ++ks) kf[ks] = k_frag<D, FP8>(X, ks);
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         s[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < Lo::KS; ++ks)
-          s[rt] = mfma_qk(__builtin_bit_cast(bf16x8_t, X.k[ks]), qf[rt][ks], s[rt]);
+        for (int ks = 0; ks < Lo::KS; ++ks) s[rt] = mfma_qk(kf[ks], qf[rt][ks], s[rt]);
       }
       sched_fence();
       const TileSrc nx = tile_at(n_next, end);
-      mload_k<D>(X, nx.k, koff);
+      mload_k<D, FP8>(X, nx.k, koff);
       sched_fence();
       // scores of tokens pos0 + 4 gq + i for this lane's row; masked past the row's limit
       float mt[RT];
@@ -336,20 +367,32 @@ __global__ __launch_bounds__(kMW * kWave, multi_waves_per_simd(D, RT)) void gqa_
         l[rt] = dot2h(p23, kOnesF16x2, l[rt]);
         p[rt] = __builtin_bit_cast(f16x4_t, uint2{p01, p23});
       }
-      // V tile -> LDS (token-major, swizzled), then refill X.v with the next tile
+      // V tile -> LDS (token-major, swizzled; FP8 codes widened to fp16 on the way), then
+      // refill X.v with the next tile
 #pragma unroll
-      for (int u = 0; u < Lo::VL; ++u) *(uint4*)(sv + vw_off[u]) = X.v[u];
+      for (int u = 0; u < Lo::VL; ++u) {
+        if constexpr (FP8) {
+          const uint4 x = X.v[u];
+          *(uint4*)(sv + vw_off[u]) = uint4{fp8x2_to_f16x2<false>(x.x), fp8x2_to_f16x2<true>(x.x),
+                                            fp8x2_to_f16x2<false>(x.y), fp8x2_to_f16x2<true>(x.y)};
+          *(uint4*)(sv + vw_off[u] + 16) = uint4{fp8x2_to_f16x2<false>(x.z), fp8x2_to_f16x2<true>(x.z),
+                                                 fp8x2_to_f16x2<false>(x.w), fp8x2_to_f16x2<true>(x.w)};
+        } else {
+          *(uint4*)(sv + vw_off[u]) = X.v[u];
+        }
+      }
       sched_fence();
-      mload_v<D>(X, nx.v, lane);
+      mload_v<D, FP8>(X, nx.v, lane);
       sched_fence();
 #pragma unroll
       for (int nt = 0; nt < Lo::NT; ++nt) {
         const uint2 raw = __builtin_bit_cast(
             uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                        (lds_s16x4_t*)(lsv + tr_base + 32 * (nt ^ tr_swz))));
-        const f16x4_t vf = __builtin_bit_cast(
-            f16x4_t, uint2{pack_f16(bf16_lo(raw.x), bf16_hi(raw.x)),
-                           pack_f16(bf16_lo(raw.y), bf16_hi(raw.y))});
+        const f16x4_t vf = FP8 ? __builtin_bit_cast(f16x4_t, raw)
+                               : __builtin_bit_cast(
+                                     f16x4_t, uint2{pack_f16(bf16_lo(raw.x), bf16_hi(raw.x)),
+                                                    pack_f16(bf16_lo(raw.y), bf16_hi(raw.y))});
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) o[rt][nt] = mfma_pv(vf, p[rt], o[rt][nt]);
       }
@@ -360,9 +403,9 @@ __global__ __launch_bounds__(kMW * kWave, multi_waves_per_simd(D, RT)) void gqa_
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const TileSrc S = tile_at(n0 + b, n1);
-      mload_k<D>(Rb[b], S.k, koff);
+      mload_k<D, FP8>(Rb[b], S.k, koff);
       sched_fence();
-      mload_v<D>(Rb[b], S.v, lane);
+      mload_v<D, FP8>(Rb[b], S.v, lane);
       sched_fence();
     }
     int n = n0;
@@ -384,7 +427,8 @@ __global__ __launch_bounds__(kMW * kWave, multi_waves_per_simd(D, RT)) void gqa_
         float* orow = a.ws_o + (slot * R + nrow) * D + 4 * gq;
 #pragma unroll
         for (int nt = 0; nt < Lo::NT; ++nt)
-          *(float4*)(orow + 16 * nt) = make_float4(o[rt][nt][0], o[rt][nt][1], o[rt][nt][2], o[rt][nt][3]);
+          *(float4*)(orow + 16 * nt) =
+              make_float4(o[rt][nt][0] * vs, o[rt][nt][1] * vs, o[rt][nt][2] * vs, o[rt][nt][3] * vs);
         if (gq == 0) {
           a.ws_m[slot * R + nrow] = m[rt];
           a.ws_l[slot * R + nrow] = lt;
@@ -450,22 +494,101 @@ __global__ __launch_bounds__(kMultiMergeWaves * kWave) void multi_merge_kernel(M
   rows_store<D>(acc, out, den > 0.f ? 1.f / den : 0.f, lane);
 }
 
-template <int D, int RT>
-static hipError_t launch_multi_one(const MultiArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((gqa_multi_kernel<D, RT>), dim3(a.chunks / kMW), dim3(kMW * kWave), 0, s, a);
+// out[b][h] = merge of the tail pieces of segment (g = h / G, b) (rows of G, from the
+// single-token balanced kernel) and the prefix pieces of segment (g, b / J), row
+// (b % J) * G + h % G (rows of J * G, from the multi-token kernel).  One wave per output row.
+template <int D>
+__global__ __launch_bounds__(kMultiMergeWaves * kWave) void cascade_merge_kernel(CascadeMergeArgs a) {
+  constexpr int PER = D / kWave;
+  const int G = a.Hq / a.Hkv;
+  const int idx = blockIdx.x * kMultiMergeWaves + (int)(threadIdx.x / kWave);
+  if (idx >= a.B * a.Hq) return;
+  const int b = idx / a.Hq, hq = idx - b * a.Hq, g = hq / G, h = hq - g * G;
+  const int lane = threadIdx.x & (kWave - 1);
+  float* out = a.out + (size_t)idx * D;
+
+  // the two piece sets: first slot, count, rows per slot, row, and liveness of each chunk
+  struct Set {
+    const float *m, *l, *o;
+    size_t slot0;
+    int np, rows, row, c0, chunks;
+    long long T;
+  };
+  auto make_set = [&](const float* m, const float* l, const float* o, const int32_t* prefix,
+                      const int32_t* segr, int chunks, int nseq, int rows, int sb, int row) {
+    Set st{m, l, o, 0, 0, rows, row, 0, chunks, 0};
+    if (!m) return st;
+    const int sg = g * nseq + sb;
+    st.c0 = segr[2 * sg];
+    st.np = segr[2 * sg + 1];
+    st.slot0 = (size_t)st.c0 + sg;
+    st.T = (long long)a.Hkv * prefix[nseq];
+    return st;
+  };
+  const Set sets[2] = {
+      make_set(a.t_m, a.t_l, a.t_o, a.t_prefix, a.t_seg, a.t_chunks, a.B, G, b, h),
+      make_set(a.p_m, a.p_l, a.p_o, a.p_prefix, a.p_seg, a.p_chunks, a.p_B, a.p_J * G,
+               a.p_J ? b / a.p_J : 0, a.p_J ? (b % a.p_J) * G + h : 0)};
+  // with fewer tiles than chunks some chunks are empty and wrote nothing
+  auto live = [](const Set& st, int i) {
+    if (st.T >= st.chunks) return true;
+    const long long cc = st.c0 + i;
+    return st.T * cc / st.chunks != st.T * (cc + 1) / st.chunks;
+  };
+  float M = kNegInf;
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    for (int p0 = 0; p0 < sets[k].np; p0 += kWave)
+      if (p0 + lane < sets[k].np && live(sets[k], p0 + lane))
+        M = fmaxf(M, sets[k].m[(sets[k].slot0 + p0 + lane) * sets[k].rows + sets[k].row]);
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) M = fmaxf(M, __shfl_xor(M, s));
+  RowAcc<D> acc;
+  rows_clear(acc);
+  float den = 0.f;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const Set& st = sets[k];
+    for (int p0 = 0; p0 < st.np; p0 += kWave) {
+      float f = 0.f, lp = 0.f;
+      if (p0 + lane < st.np && live(st, p0 + lane)) {
+        const size_t si = (st.slot0 + p0 + lane) * st.rows + st.row;
+        const float mp = st.m[si];
+        lp = st.l[si];
+        f = (mp == kNegInf) ? 0.f : fast_exp2(mp - M);
+      }
+      float fl = f * lp;
+#pragma unroll
+      for (int s = 32; s >= 1; s >>= 1) fl += __shfl_xor(fl, s);
+      den += fl;
+      rows_accumulate<D>(acc, st.o + ((st.slot0 + p0) * st.rows + st.row) * D,
+                         (size_t)st.rows * D, f, min(kWave, st.np - p0), lane);
+    }
+  }
+  if (den == 0.f) {  // no token at all
+#pragma unroll
+    for (int i = 0; i < PER; ++i) out[lane + kWave * i] = 0.f;
+    return;
+  }
+  rows_store<D>(acc, out, 1.f / den, lane);
+}
+
+template <int D, int RT, bool FP8>
+static hipError_t launch_multi_one(const MultiArgs& a, hipStream_t s, bool merge) {
+  hipLaunchKernelGGL((gqa_multi_kernel<D, RT, FP8>), dim3(a.chunks / kMW), dim3(kMW * kWave), 0, s, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !merge) return e;
   const dim3 grid((unsigned)(((long long)a.B * a.q_len * a.Hq + kMultiMergeWaves - 1) / kMultiMergeWaves));
   hipLaunchKernelGGL(multi_merge_kernel<D>, grid, dim3(kMultiMergeWaves * kWave), 0, s, a);
   return hipGetLastError();
 }
 
-template <int D>
-static hipError_t launch_multi_d(const MultiArgs& a, hipStream_t s) {
+template <int D, bool FP8>
+static hipError_t launch_multi_d(const MultiArgs& a, hipStream_t s, bool merge) {
   const int R = a.Hq / a.Hkv * a.q_len;
-  if (R <= 16) return launch_multi_one<D, 1>(a, s);
-  if (R <= 32) return launch_multi_one<D, 2>(a, s);
-  if (R <= 64) return launch_multi_one<D, 4>(a, s);
+  if (R <= 16) return launch_multi_one<D, 1, FP8>(a, s, merge);
+  if (R <= 32) return launch_multi_one<D, 2, FP8>(a, s, merge);
+  if (R <= 64) return launch_multi_one<D, 4, FP8>(a, s, merge);
   return hipErrorInvalidValue;
 }
 
@@ -475,11 +598,25 @@ int multi_waves_per_cu(int d, int rows) {
   return kMW * multi_waves_per_simd(64, rt);
 }
 
-hipError_t launch_gqa_multi(const MultiArgs& a, hipStream_t s) {
+static hipError_t launch_multi_impl(const MultiArgs& a, hipStream_t s, bool merge) {
   if (a.B > kMultiSeqs || a.chunks % 32 || a.block_size % kTile) return hipErrorInvalidValue;
-  if (a.d == 128) return launch_multi_d<128>(a, s);
-  if (a.d == 64) return launch_multi_d<64>(a, s);
+  if (a.d == 128) return a.fp8 ? launch_multi_d<128, true>(a, s, merge) : launch_multi_d<128, false>(a, s, merge);
+  if (a.d == 64) return a.fp8 ? launch_multi_d<64, true>(a, s, merge) : launch_multi_d<64, false>(a, s, merge);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gqa_multi(const MultiArgs& a, hipStream_t s) { return launch_multi_impl(a, s, true); }
+
+hipError_t launch_gqa_multi_pieces(const MultiArgs& a, hipStream_t s) {
+  return launch_multi_impl(a, s, false);
+}
+
+hipError_t launch_cascade_merge(const CascadeMergeArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(((long long)a.B * a.Hq + kMultiMergeWaves - 1) / kMultiMergeWaves));
+  if (a.d == 128) hipLaunchKernelGGL(cascade_merge_kernel<128>, grid, dim3(kMultiMergeWaves * kWave), 0, s, a);
+  else if (a.d == 64) hipLaunchKernelGGL(cascade_merge_kernel<64>, grid, dim3(kMultiMergeWaves * kWave), 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace pkv

@@ -285,21 +285,21 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void stream_merge_kernel(Decod
 }
 
 template <int D, int G, bool FP8>
-static hipError_t launch_stream_one(const DecodeArgs& a, hipStream_t s) {
+static hipError_t launch_stream_one(const DecodeArgs& a, hipStream_t s, bool merge) {
   hipLaunchKernelGGL((gqa_stream_kernel<D, G, FP8>), dim3(a.chunks / kWaves), dim3(kWaves * kWave),
                      0, s, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !merge) return e;
   return launch_stream_merge(a, s);
 }
 
 template <int D, bool FP8>
-static hipError_t launch_stream_d(const DecodeArgs& a, hipStream_t s) {
+static hipError_t launch_stream_d(const DecodeArgs& a, hipStream_t s, bool merge) {
   switch (a.Hq / a.Hkv) {
-    case 1: return launch_stream_one<D, 1, FP8>(a, s);
-    case 2: return launch_stream_one<D, 2, FP8>(a, s);
-    case 4: return launch_stream_one<D, 4, FP8>(a, s);
-    case 8: return launch_stream_one<D, 8, FP8>(a, s);
+    case 1: return launch_stream_one<D, 1, FP8>(a, s, merge);
+    case 2: return launch_stream_one<D, 2, FP8>(a, s, merge);
+    case 4: return launch_stream_one<D, 4, FP8>(a, s, merge);
+    case 8: return launch_stream_one<D, 8, FP8>(a, s, merge);
     default: return hipErrorInvalidValue;
   }
 }
@@ -313,11 +313,20 @@ hipError_t launch_stream_merge(const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gqa_stream(const DecodeArgs& a, hipStream_t s) {
+static hipError_t launch_gqa_stream_impl(const DecodeArgs& a, hipStream_t s, bool merge) {
   if (a.B > kMaxStreamSeqs || a.chunks % 32) return hipErrorInvalidValue;
-  if (a.d == 128) return a.fp8 ? launch_stream_d<128, true>(a, s) : launch_stream_d<128, false>(a, s);
-  if (a.d == 64 && !a.fp8) return launch_stream_d<64, false>(a, s);
+  if (a.d == 128)
+    return a.fp8 ? launch_stream_d<128, true>(a, s, merge) : launch_stream_d<128, false>(a, s, merge);
+  if (a.d == 64 && !a.fp8) return launch_stream_d<64, false>(a, s, merge);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gqa_stream(const DecodeArgs& a, hipStream_t s) {
+  return launch_gqa_stream_impl(a, s, true);
+}
+
+hipError_t launch_gqa_stream_pieces(const DecodeArgs& a, hipStream_t s) {
+  return launch_gqa_stream_impl(a, s, false);
 }
 
 }  // namespace pkv

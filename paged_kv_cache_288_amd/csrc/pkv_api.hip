@@ -154,6 +154,45 @@ int32_t multi_chunks(int32_t B, int32_t q_len, int32_t Hq, int32_t Hkv, int32_t 
                        pkv::multi_waves_per_cu(d, (Hq / Hkv) * q_len));
 }
 
+// Multi-token workspace sections (m, l, o, tile prefix, segment ranges) into a.
+void multi_ws_split(void* ws, int32_t B, int32_t q_len, int32_t Hq, int32_t Hkv, int32_t d,
+                    int32_t chunks, pkv::MultiArgs& a) {
+  const size_t rows = ((size_t)chunks + (size_t)Hkv * B) * (size_t)(Hq / Hkv) * q_len;
+  char* base = (char*)ws;
+  a.ws_m = (float*)base;
+  a.ws_l = (float*)(base + round256(rows * sizeof(float)));
+  a.ws_o = (float*)(base + 2 * round256(rows * sizeof(float)));
+  a.ws_prefix = (int32_t*)(base + 2 * round256(rows * sizeof(float)) +
+                           round256(rows * d * sizeof(float)));
+  a.ws_seg = (int32_t*)((char*)a.ws_prefix + round256(((size_t)B + 1) * sizeof(int32_t)));
+}
+
+// Cascade call: the tail pass's balanced workspace, then the prefix pass's multi-token
+// workspace for groups of J = 64 / G sequences (64 query rows per KV head and group).
+struct CascadePlan {
+  bool ok;
+  int32_t t_chunks, p_chunks, J, p_B;
+  size_t t_bytes, p_bytes;
+};
+CascadePlan cascade_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t prefix_len,
+                         int32_t max_tail_len) {
+  CascadePlan c{false, 0, 0, 0, 0, 0, 0};
+  const int32_t G = Hq / Hkv;
+  if (G < 1 || G > 64) return c;
+  c.t_chunks = stream_chunks(B, Hkv, max_tail_len);
+  if (c.t_chunks < 0) return c;
+  c.t_bytes = stream_ws_bytes(B, Hq, Hkv, d, c.t_chunks);
+  c.J = 64 / G;
+  c.p_B = (B + c.J - 1) / c.J;
+  if (prefix_len > 0) {
+    c.p_chunks = multi_chunks(c.p_B, c.J, Hq, Hkv, d, prefix_len);
+    if (c.p_chunks < 0) return c;
+    c.p_bytes = multi_ws_bytes(c.p_B, c.J, Hq, Hkv, d, c.p_chunks);
+  }
+  c.ok = true;
+  return c;
+}
+
 bool multi_shape_ok(int32_t B, int32_t q_len, int32_t Hq, int32_t Hkv, int32_t d,
                     int32_t max_context_len) {
   return B >= 0 && q_len > 0 && Hq > 0 && Hkv > 0 && Hq % Hkv == 0 && d > 0 &&
@@ -371,7 +410,8 @@ size_t pkv_multi_workspace_bytes(int32_t B, int32_t q_len, int32_t Hq, int32_t H
 }
 
 pkv_status pkv_paged_decode_attn_multi(float* out, const void* q, const void* k_pool,
-                                       const void* v_pool, const int32_t* block_table,
+                                       const void* v_pool, const float* k_scale,
+                                       const float* v_scale, const int32_t* block_table,
                                        const int32_t* context_lens, int32_t B, int32_t q_len,
                                        int32_t Hq, int32_t Hkv, int32_t d, int32_t block_size,
                                        int32_t num_blocks, int32_t max_blocks_per_seq,
@@ -383,11 +423,13 @@ pkv_status pkv_paged_decode_attn_multi(float* out, const void* q, const void* k_
   if (!elem_bytes(kv_dtype)) return PKV_ERR_DTYPE;
   if (B == 0) return PKV_OK;
   if (!out || !q || !k_pool || !v_pool || !block_table || !context_lens) return PKV_ERR_NULL;
-  if (kv_dtype != PKV_BF16 || (d != 128 && d != 64) || block_size % 16 ||
-      (long long)(Hq / Hkv) * q_len > 64)
+  const bool fp8 = kv_dtype == PKV_FP8_E4M3;
+  if (fp8 && (!k_scale || !v_scale)) return PKV_ERR_NULL;
+  if ((d != 128 && d != 64) || block_size % 16 || (long long)(Hq / Hkv) * q_len > 64)
     return PKV_ERR_UNSUPPORTED;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
-      !aligned4(block_table) || !aligned4(context_lens))
+      !aligned4(block_table) || !aligned4(context_lens) ||
+      (fp8 && (!aligned4(k_scale) || !aligned4(v_scale))))
     return PKV_ERR_ALIGN;
   if (B > kMaxStreamSeqs || (long long)Hkv * B >= (1LL << 26)) return PKV_ERR_SHAPE;
   const int32_t chunks = multi_chunks(B, q_len, Hq, Hkv, d, max_context_len);
@@ -395,19 +437,105 @@ pkv_status pkv_paged_decode_attn_multi(float* out, const void* q, const void* k_
   if (!workspace || workspace_bytes < multi_ws_bytes(B, q_len, Hq, Hkv, d, chunks))
     return PKV_ERR_WORKSPACE;
   if (!aligned16(workspace)) return PKV_ERR_ALIGN;
-  const size_t rows = ((size_t)chunks + (size_t)Hkv * B) * (size_t)(Hq / Hkv) * q_len;
-  char* base = (char*)workspace;
-  float* ws_m = (float*)base;
-  float* ws_l = (float*)(base + round256(rows * sizeof(float)));
-  float* ws_o = (float*)(base + 2 * round256(rows * sizeof(float)));
-  int32_t* ws_p = (int32_t*)(base + 2 * round256(rows * sizeof(float)) +
-                             round256(rows * d * sizeof(float)));
-  int32_t* ws_s = (int32_t*)((char*)ws_p + round256(((size_t)B + 1) * sizeof(int32_t)));
-  pkv::MultiArgs a{out, (const uint16_t*)q, (const uint8_t*)k_pool, (const uint8_t*)v_pool,
-                   block_table, context_lens, ws_m, ws_l, ws_o, ws_p, ws_s,
-                   B, q_len, Hq, Hkv, d, block_size, num_blocks, max_blocks_per_seq,
-                   scale, chunks};
+  pkv::MultiArgs a{};
+  multi_ws_split(workspace, B, q_len, Hq, Hkv, d, chunks, a);
+  a.out = out;
+  a.q = (const uint16_t*)q;
+  a.k_pool = (const uint8_t*)k_pool;
+  a.v_pool = (const uint8_t*)v_pool;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.B = B, a.q_len = q_len, a.Hq = Hq, a.Hkv = Hkv, a.d = d, a.block_size = block_size;
+  a.num_blocks = num_blocks, a.max_blocks = max_blocks_per_seq;
+  a.table_stride = max_blocks_per_seq, a.fixed_len = -1, a.q_rows = B * q_len;
+  a.causal = 1, a.fp8 = fp8 ? 1 : 0, a.scale = scale, a.chunks = chunks;
   return hip_status(pkv::launch_gqa_multi(a, (hipStream_t)stream));
+}
+
+size_t pkv_cascade_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                                   int32_t prefix_len, int32_t max_tail_len) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || d <= 0 || prefix_len < 0 || max_tail_len < 0)
+    return 0;
+  const CascadePlan c = cascade_plan(B, Hq, Hkv, d, prefix_len, max_tail_len);
+  return c.ok ? c.t_bytes + c.p_bytes : 0;
+}
+
+pkv_status pkv_paged_decode_attn_cascade(float* out, const void* q, const void* k_pool,
+                                         const void* v_pool, const float* k_scale,
+                                         const float* v_scale, const int32_t* prefix_blocks,
+                                         int32_t prefix_len, const int32_t* tail_table,
+                                         const int32_t* tail_lens, int32_t B, int32_t Hq,
+                                         int32_t Hkv, int32_t d, int32_t block_size,
+                                         int32_t num_blocks, int32_t max_tail_blocks,
+                                         int32_t max_tail_len, float scale, int32_t kv_dtype,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || block_size <= 0 || num_blocks <= 0 ||
+      max_tail_blocks <= 0 || max_tail_len < 0 || prefix_len < 0)
+    return PKV_ERR_SHAPE;
+  if (Hq % Hkv || prefix_len % block_size) return PKV_ERR_SHAPE;
+  if (!elem_bytes(kv_dtype)) return PKV_ERR_DTYPE;
+  if (B == 0) return PKV_OK;
+  if (!out || !q || !k_pool || !v_pool || !tail_table || !tail_lens ||
+      (prefix_len > 0 && !prefix_blocks))
+    return PKV_ERR_NULL;
+  const bool fp8 = kv_dtype == PKV_FP8_E4M3;
+  if (fp8 && (!k_scale || !v_scale)) return PKV_ERR_NULL;
+  const int32_t G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PKV_ERR_UNSUPPORTED;
+  if (!((d == 128) || (d == 64 && !fp8)) || block_size % 16) return PKV_ERR_UNSUPPORTED;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      !aligned4(tail_table) || !aligned4(tail_lens) || (prefix_len > 0 && !aligned4(prefix_blocks)) ||
+      (fp8 && (!aligned4(k_scale) || !aligned4(v_scale))))
+    return PKV_ERR_ALIGN;
+  if (B > kMaxStreamSeqs || (long long)Hkv * B >= (1LL << 26)) return PKV_ERR_SHAPE;
+  const CascadePlan c = cascade_plan(B, Hq, Hkv, d, prefix_len, max_tail_len);
+  if (!c.ok) return PKV_ERR_SHAPE;
+  if (!workspace || workspace_bytes < c.t_bytes + c.p_bytes) return PKV_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+
+  // tails: the single-token balanced kernel over each sequence's own blocks, pieces only
+  const size_t rows = ((size_t)c.t_chunks + (size_t)Hkv * B) * (size_t)G;
+  char* base = (char*)workspace;
+  float* t_m = (float*)base;
+  float* t_l = (float*)(base + round256(rows * sizeof(float)));
+  float* t_o = (float*)(base + 2 * round256(rows * sizeof(float)));
+  int32_t* t_p = (int32_t*)(base + 2 * round256(rows * sizeof(float)) + round256(rows * d * sizeof(float)));
+  int32_t* t_s = (int32_t*)((char*)t_p + round256(((size_t)B + 1) * sizeof(int32_t)));
+  pkv::DecodeArgs ta{out, (const uint16_t*)q, (const uint8_t*)k_pool, (const uint8_t*)v_pool,
+                     k_scale, v_scale, tail_table, tail_lens, t_m, t_l, t_o,
+                     B, Hq, Hkv, d, block_size, num_blocks, max_tail_blocks, max_tail_len,
+                     0, 0, scale, fp8 ? 1 : 0, c.t_chunks, t_p, t_s};
+  pkv_status st = hip_status(pkv::launch_gqa_stream_pieces(ta, s));
+  if (st != PKV_OK) return st;
+
+  // prefix: groups of J sequences as the q_len rows of the multi-token kernel, all reading
+  // the prefix blocks, no causal mask
+  pkv::MultiArgs pa{};
+  if (prefix_len > 0) {
+    multi_ws_split(base + c.t_bytes, c.p_B, c.J, Hq, Hkv, d, c.p_chunks, pa);
+    pa.out = nullptr;
+    pa.q = (const uint16_t*)q;
+    pa.k_pool = (const uint8_t*)k_pool;
+    pa.v_pool = (const uint8_t*)v_pool;
+    pa.k_scale = k_scale;
+    pa.v_scale = v_scale;
+    pa.block_table = prefix_blocks;
+    pa.context_lens = nullptr;
+    pa.B = c.p_B, pa.q_len = c.J, pa.Hq = Hq, pa.Hkv = Hkv, pa.d = d;
+    pa.block_size = block_size, pa.num_blocks = num_blocks;
+    pa.max_blocks = prefix_len / block_size, pa.table_stride = 0, pa.fixed_len = prefix_len;
+    pa.q_rows = B, pa.causal = 0, pa.fp8 = fp8 ? 1 : 0, pa.scale = scale, pa.chunks = c.p_chunks;
+    st = hip_status(pkv::launch_gqa_multi_pieces(pa, s));
+    if (st != PKV_OK) return st;
+  }
+
+  pkv::CascadeMergeArgs ma{out, B, Hq, Hkv, d, t_m, t_l, t_o, t_p, t_s, c.t_chunks,
+                           prefix_len > 0 ? pa.ws_m : nullptr, pa.ws_l, pa.ws_o, pa.ws_prefix,
+                           pa.ws_seg, c.p_chunks, c.p_B, c.J};
+  return hip_status(pkv::launch_cascade_merge(ma, s));
 }
 
 pkv_status pkv_kv_append_fp8(void* k_pool, void* v_pool, const void* k_new, const void* v_new,

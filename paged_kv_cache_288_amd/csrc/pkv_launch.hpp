@@ -101,26 +101,57 @@ int mla_stream_heads_per_group(int Hq);
 hipError_t launch_mla_stream(const MlaArgs& a, hipStream_t s);
 
 // Multi-token decode (q_len query tokens per sequence, causal among them), balanced mode
-// only.  Row n of segment (g, b) is query token n / G, head g * G + n % G.
+// only.  Row n of segment (g, b) is query token n / G, head g * G + n % G.  The same kernel
+// serves the shared-prefix pass of the cascade call: there the "sequences" are groups of
+// q_len real sequences (q row b * q_len + j is real sequence b * q_len + j), all of them
+// reading the same block-table row (table_stride 0) of fixed_len tokens, without the
+// causal mask.
 struct MultiArgs {
-  float* out;           // [B][q_len][Hq][d]
+  float* out;           // [B][q_len][Hq][d] (merged output; unused when only pieces are made)
   const uint16_t* q;    // [B][q_len][Hq][d] bf16
   const uint8_t* k_pool;
   const uint8_t* v_pool;
-  const int32_t* block_table;
-  const int32_t* context_lens;
+  const float* k_scale;  // [Hkv] (FP8) or null
+  const float* v_scale;
+  const int32_t* block_table;   // row b at b * table_stride
+  const int32_t* context_lens;  // [B], unused when fixed_len >= 0
   float* ws_m;  // [S][R], S = chunks + Hkv * B piece slots, R = q_len * Hq / Hkv rows
   float* ws_l;  // [S][R]
   float* ws_o;  // [S][R][d]
   int32_t* ws_prefix;  // [B + 1]
   int32_t* ws_seg;     // [Hkv * B][2]
-  int32_t B, q_len, Hq, Hkv, d, block_size, num_blocks, max_blocks;
+  int32_t B, q_len, Hq, Hkv, d, block_size, num_blocks;
+  int32_t max_blocks;    // valid table entries per sequence
+  int32_t table_stride;  // elements between table rows (0: one row shared by all)
+  int32_t fixed_len;     // >= 0: every sequence has this length
+  int32_t q_rows;        // real q rows along (b, j): B * q_len, fewer in prefix mode
+  int32_t causal, fp8;
   float scale;
-  int32_t chunks;  // one per wave, a multiple of 32
+  int32_t chunks;  // one per resident wave, a multiple of 32
 };
 // Decode kernel + merge kernel.
 hipError_t launch_gqa_multi(const MultiArgs& a, hipStream_t s);
+// Decode kernel only: pieces, tile prefix and segment ranges in the workspace.
+hipError_t launch_gqa_multi_pieces(const MultiArgs& a, hipStream_t s);
 // Resident waves per CU of the multi-token decode kernel for head dim d and q_len * G rows.
 int multi_waves_per_cu(int d, int rows);
+
+// Balanced-mode single-token decode kernel only (pieces for a later merge).
+hipError_t launch_gqa_stream_pieces(const DecodeArgs& a, hipStream_t s);
+
+// Cascade merge: out[b][h] combines the tail pieces of (h / G, b) from the single-token
+// balanced kernel with the prefix pieces of row (b % J) * G + h % G of segment
+// (h / G, b / J) from the multi-token kernel (J = q_len of the prefix pass).
+struct CascadeMergeArgs {
+  float* out;  // [B][Hq][d]
+  int32_t B, Hq, Hkv, d;
+  const float *t_m, *t_l, *t_o;          // tail pieces: rows of G
+  const int32_t *t_prefix, *t_seg;
+  int32_t t_chunks;
+  const float *p_m, *p_l, *p_o;          // prefix pieces: rows of J * G (null: no prefix)
+  const int32_t *p_prefix, *p_seg;
+  int32_t p_chunks, p_B, p_J;
+};
+hipError_t launch_cascade_merge(const CascadeMergeArgs& a, hipStream_t s);
 
 }  // namespace pkv

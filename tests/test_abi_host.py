@@ -262,26 +262,27 @@ def test_quantizing_append_and_block_copy_reject_bad_arguments(lib):
 
 def test_multi_rejects_bad_arguments_before_launch(lib):
     f = lib.pkv_paged_decode_attn_multi
-    # out q k v bt cl B q_len Hq Hkv d bs nb mb ctx scale dtype ws wsb stream
-    base = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 64, 8, 128, 16, 10, 4, 64, 0.1,
-            pkv.PKV_BF16, None, 0, None]
+    # out q k v ks vs bt cl B q_len Hq Hkv d bs nb mb ctx scale dtype ws wsb stream
+    base = [FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 2, 4, 64, 8, 128, 16, 10, 4, 64,
+            0.1, pkv.PKV_BF16, None, 0, None]
     def call(**kw):
         a = list(base)
         for i, v in kw.items():
             a[int(i[1:])] = v
         return f(*a)
-    assert call(a7=0) == -2              # q_len
-    assert call(a8=60) == -2             # Hq not a multiple of Hkv
-    assert call(a16=9) == -3
-    assert call(a6=0) == 0               # empty batch
+    assert call(a9=0) == -2              # q_len
+    assert call(a10=60) == -2            # Hq not a multiple of Hkv
+    assert call(a18=9) == -3
+    assert call(a8=0) == 0               # empty batch
     assert call(a0=None) == -1
-    assert call(a7=9) == -4              # 72 rows per KV head
-    assert call(a16=pkv.PKV_FP8_E4M3) == -4
-    assert call(a10=96) == -4
-    assert call(a11=8) == -4
+    assert call(a18=pkv.PKV_FP8_E4M3) == -1   # FP8 needs its scales
+    assert call(a9=9) == -4              # 72 rows per KV head
+    assert call(a12=96) == -4
+    assert call(a13=8) == -4
     assert call(a1=MIS) == -5
     assert call() == -6                  # needs a workspace
-    assert call(a17=FAKE, a18=64) == -6
+    assert call(a19=FAKE, a20=64) == -6
+    assert call(a18=pkv.PKV_FP8_E4M3, a4=FAKE, a5=FAKE) == -6
 
 
 def test_multi_workspace_size(lib):
@@ -299,3 +300,49 @@ def test_multi_workspace_size(lib):
         assert lib.pkv_multi_workspace_bytes(B, q_len, Hq, Hkv, d, ctx) == want
     assert lib.pkv_multi_workspace_bytes(2, 9, 64, 8, 128, 100) == 0     # 72 rows
     assert lib.pkv_multi_workspace_bytes(2, 0, 64, 8, 128, 100) == 0
+
+
+def test_cascade_rejects_bad_arguments_before_launch(lib):
+    f = lib.pkv_paged_decode_attn_cascade
+    # out q k v ks vs prefix plen tail_t tail_l B Hq Hkv d bs nb mtb mtl scale dtype ws wsb stream
+    base = [FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 64, FAKE, FAKE, 4, 32, 8, 128, 16, 100,
+            8, 128, 0.1, pkv.PKV_BF16, None, 0, None]
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a7=40) == -2               # prefix not whole blocks
+    assert call(a11=30) == -2              # Hq not a multiple of Hkv
+    assert call(a16=0) == -2
+    assert call(a19=5) == -3
+    assert call(a10=0) == 0
+    assert call(a6=None) == -1             # prefix_len > 0 needs its blocks
+    assert call(a19=pkv.PKV_FP8_E4M3) == -1
+    assert call(a11=128) == -4             # G = 16
+    assert call(a13=64, a19=pkv.PKV_FP8_E4M3, a4=FAKE, a5=FAKE) == -4
+    assert call(a1=MIS) == -5
+    assert call() == -6
+    assert call(a6=None, a7=0) == -6       # no prefix is fine, the workspace is still needed
+
+
+def test_cascade_workspace_size(lib):
+    """Tail pass (balanced, rows of G) then prefix pass (multi-token, 64 / G sequences per
+    group, 64 rows); 256 CUs assumed without a GPU."""
+    r256 = lambda x: (x + 255) // 256 * 256
+    def chunks(tiles, waves):
+        c = max(min(waves * 256, tiles), -(-tiles // 128))
+        return max(32, -(-c // 32) * 32)
+    for B, Hq, Hkv, d, plen, tmax in [(128, 32, 8, 128, 4096, 2048), (37, 8, 8, 128, 320, 401),
+                                      (9, 4, 1, 64, 0, 90), (5, 64, 8, 128, 512, 0)]:
+        G = Hq // Hkv
+        ct = chunks(Hkv * B * -(-tmax // 16), 8)
+        rows = (ct + Hkv * B) * G
+        want = 2 * r256(rows * 4) + r256(rows * d * 4) + r256((B + 1) * 4) + r256(Hkv * B * 8)
+        if plen:
+            J = 64 // G
+            pB = -(-B // J)
+            cp = chunks(Hkv * pB * -(-plen // 16), 4 if d * 4 > 256 else 8)
+            prow = (cp + Hkv * pB) * 64
+            want += 2 * r256(prow * 4) + r256(prow * d * 4) + r256((pB + 1) * 4) + r256(Hkv * pB * 8)
+        assert lib.pkv_cascade_workspace_bytes(B, Hq, Hkv, d, plen, tmax) == want, (B, Hq)

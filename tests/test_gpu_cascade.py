@@ -1,0 +1,100 @@
+"""GPU parity of pkv_paged_decode_attn_cascade (shared-prefix decode) through the C-ABI
+against the fp64 oracle, which attends over each sequence's whole block table (prefix
+blocks followed by the tail blocks): the cascade must give the plain result.
+
+Covered: the FP8 shared-prefix workload reduced and at full size (sampled), bf16, every
+group size the kernels take (the prefix pass then packs 64 / G sequences per row group,
+including a ragged last group), head dim 64, no prefix at all, empty tails, and a prefix
+that is the whole context."""
+
+import numpy as np
+import pytest
+
+from gpu_common import assert_close, bits_to_device, log, make_workload, oracle_decode, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+def split_prefix(w, prefix_blocks=None):
+    """Prefix block ids, tail table and tail lengths of a workload whose first
+    prefix_blocks table entries are shared by every sequence."""
+    pb = w.meta["prefix_blocks"] if prefix_blocks is None else prefix_blocks
+    prefix = w.block_table[0, :pb].astype(np.int32)
+    assert (w.block_table[:, :pb] == prefix[None, :]).all()
+    tail_table = np.ascontiguousarray(w.block_table[:, pb:])
+    if tail_table.shape[1] == 0:
+        tail_table = np.full((w.B, 1), -1, dtype=np.int32)
+    tail_lens = (w.context_lens - pb * w.bs).astype(np.int32)
+    assert (tail_lens >= 0).all()
+    return prefix, pb * w.bs, tail_table, tail_lens
+
+
+def gpu_cascade(torch, w, prefix_blocks=None):
+    import paged_kv_cache_288_amd as pkv
+    prefix, plen, tail_table, tail_lens = split_prefix(w, prefix_blocks)
+    dev = "cuda"
+    out = torch.empty((w.B, w.Hq, w.d_v), dtype=torch.float32, device=dev)
+    ks = None if w.k_scale is None else torch.from_numpy(w.k_scale).to(dev)
+    vs = None if w.v_scale is None else torch.from_numpy(w.v_scale).to(dev)
+    pkv.paged_decode_attn_cascade(
+        out, bits_to_device(torch, w.q), bits_to_device(torch, w.k_pool),
+        bits_to_device(torch, w.v_pool),
+        torch.from_numpy(prefix).to(dev) if len(prefix) else None, plen,
+        torch.from_numpy(tail_table).to(dev), torch.from_numpy(tail_lens).to(dev), w.scale,
+        int(tail_lens.max()) if w.B else 0, kv_dtype=w.kv_dtype, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_cascade_fp8_prefix_reduced(seed):
+    torch = torch_cuda()
+    w = make_workload("fp8prefix", seed=seed, B=20, lens=("prefix", 512, 0, 700))
+    log(f"[cascade] fp8 seed={seed} prefix={w.meta['prefix_blocks']} blocks "
+        f"lens={w.context_lens.tolist()}")
+    assert_close(gpu_cascade(torch, w), oracle_decode(w), "fp8", f"fp8 prefix/{seed}")
+
+
+@pytest.mark.parametrize("heads", [(8, 8), (16, 8), (32, 8), (64, 8), (4, 1)])
+def test_cascade_group_sizes_bf16(heads):
+    """bf16 K/V (the FP8 workload's structure with bf16 storage); group sizes 1..8, so the
+    prefix pass packs 64, 32, 16 or 8 sequences per row group (B = 37: a ragged group)."""
+    torch = torch_cuda()
+    w = make_workload("gqa70b", seed=3, B=37, lens=("prefix", 320, 1, 400), heads=heads)
+    assert w.meta["prefix_blocks"] == 20
+    log(f"[cascade] bf16 heads={heads} lens={w.context_lens.tolist()[:10]}...")
+    assert_close(gpu_cascade(torch, w), oracle_decode(w), "bf16", f"bf16 heads {heads}")
+
+
+def test_cascade_head_dim_64():
+    torch = torch_cuda()
+    w = make_workload("tiny", seed=2, B=9, lens=("prefix", 160, 0, 90), pool=("factor", 1.25))
+    assert_close(gpu_cascade(torch, w), oracle_decode(w), "bf16", "d=64")
+
+
+def test_cascade_without_prefix_and_with_empty_tails():
+    torch = torch_cuda()
+    w = make_workload("gqa70b", seed=8, B=6, lens=("prefix", 256, 0, 300))
+    w.context_lens[[1, 4]] = 256                       # tails of length 0
+    ref = oracle_decode(w)
+    assert_close(gpu_cascade(torch, w), ref, "bf16", "empty tails")
+    # the same sequences with no shared prefix: every block is a tail block
+    assert_close(gpu_cascade(torch, w, prefix_blocks=0), ref, "bf16", "no prefix")
+
+
+def test_cascade_prefix_is_whole_context():
+    torch = torch_cuda()
+    w = make_workload("gqa70b", seed=9, B=5, lens=("prefix", 512, 0, 0))
+    assert (w.context_lens == 512).all()
+    assert_close(gpu_cascade(torch, w), oracle_decode(w), "bf16", "prefix only")
+
+
+def test_cascade_full_size_sampled():
+    """The 128-sequence FP8 shared-prefix workload as benchmarked."""
+    torch = torch_cuda()
+    w = make_workload("fp8prefix")
+    log(f"[cascade] full size {w.name}: B={w.B} max_ctx={w.max_context_len}")
+    got = gpu_cascade(torch, w)
+    seqs = sorted(np.random.default_rng(77).choice(w.B, size=8, replace=False).tolist())
+    assert_close(got[seqs], oracle_decode(w, seqs), "fp8", f"fp8prefix cascade sampled {seqs}")
+    assert np.isfinite(got).all()

@@ -26,7 +26,10 @@ def gpu_multi(torch, w, out=None):
     cl = torch.from_numpy(w.context_lens).to("cuda")
     if out is None:
         out = torch.empty((w.B, w.q_len, w.Hq, w.d_v), dtype=torch.float32, device="cuda")
-    pkv.paged_decode_attn_multi(out, q, kp, vp, bt, cl, w.scale, w.max_context_len)
+    ks = None if w.k_scale is None else torch.from_numpy(w.k_scale).to("cuda")
+    vs = None if w.v_scale is None else torch.from_numpy(w.v_scale).to("cuda")
+    pkv.paged_decode_attn_multi(out, q, kp, vp, bt, cl, w.scale, w.max_context_len,
+                                kv_dtype=w.kv_dtype, k_scale=ks, v_scale=vs)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -35,8 +38,8 @@ def oracle_multi(w, seqs=None):
     seqs = range(w.B) if seqs is None else list(seqs)
     kp, vp, table, lens, _ = _subset(w, seqs)
     q = oracle.bf16_bits_to_f64(w.q.reshape(w.B, w.q_len, w.Hq, w.d)[list(seqs)])
-    K = oracle.decode_kv_bits(kp, "bf16")
-    V = oracle.decode_kv_bits(vp, "bf16")
+    K = oracle.decode_kv_bits(kp, w.kv_dtype, w.k_scale)
+    V = oracle.decode_kv_bits(vp, w.kv_dtype, w.v_scale)
     return oracle.multi_token_decode_attention(q, K, V, table, lens, w.scale)
 
 
@@ -63,6 +66,16 @@ def test_multi_row_counts(heads, q_len):
                       q_len=q_len)
     log(f"[multi] heads={heads} q_len={q_len} lens={w.context_lens.tolist()}")
     assert_close(gpu_multi(torch, w), oracle_multi(w), "bf16", f"heads {heads} q_len {q_len}")
+
+
+@pytest.mark.parametrize("q_len,heads", [(4, (32, 8)), (2, (64, 8)), (16, (32, 8))])
+def test_multi_fp8(q_len, heads):
+    """FP8 E4M3 K/V with per-head scales (codes widened exactly on the way to the MFMA)."""
+    torch = torch_cuda()
+    w = make_workload("fp8prefix", seed=6, B=5, lens=("prefix", 64, 1, 700), q_len=q_len,
+                      heads=heads)
+    log(f"[multi] fp8 q_len={q_len} heads={heads} lens={w.context_lens.tolist()}")
+    assert_close(gpu_multi(torch, w), oracle_multi(w), "fp8", f"fp8 q_len={q_len}")
 
 
 def test_multi_short_and_empty_contexts():
