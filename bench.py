@@ -41,6 +41,8 @@ KERNEL_SOURCES = {
             "paged_kv_cache_288_amd/csrc/gqa_tile.hpp", "paged_kv_cache_288_amd/csrc/pkv_device.hpp"],
     "multi": ["paged_kv_cache_288_amd/csrc/gqa_multi.hip", "paged_kv_cache_288_amd/csrc/gqa_tile.hpp",
               "paged_kv_cache_288_amd/csrc/pkv_device.hpp"],
+    "cascade": ["paged_kv_cache_288_amd/csrc/gqa_stream.hip", "paged_kv_cache_288_amd/csrc/gqa_multi.hip",
+                "paged_kv_cache_288_amd/csrc/gqa_tile.hpp", "paged_kv_cache_288_amd/csrc/pkv_device.hpp"],
 }
 
 
@@ -74,6 +76,15 @@ def kv_bytes(w):
     return int(w.context_lens.astype(np.int64).sum()) * per_token
 
 
+def kv_unique_bytes(w):
+    """KV bytes stored for the batch: a shared prefix counted once, then every sequence's
+    own tokens (what has to come from HBM at least once per call)."""
+    per_token = kv_bytes(w) // max(int(w.context_lens.astype(np.int64).sum()), 1)
+    prefix = w.meta.get("prefix_blocks", 0) * w.bs
+    own = int((w.context_lens.astype(np.int64) - prefix).sum())
+    return (prefix + own) * per_token
+
+
 def traffic_for(workload_name, kind):
     """Measured HBM bytes per call from committed counter runs, if they were taken on
     the current kernel source; otherwise None."""
@@ -96,7 +107,10 @@ def kernel_family(w):
     return "multi" if w.q_len > 1 else "gqa"
 
 
-def kernel_label(w, pkv, ps):
+def kernel_label(w, pkv, ps, cascade=False):
+    if cascade:
+        return ("pkv_paged_decode_attn_cascade call (gqa_stream_kernel over the tails, "
+                "gqa_multi_kernel over the shared prefix, cascade_merge_kernel)")
     if w.q_len > 1:
         return "pkv_paged_decode_attn_multi call (gqa_multi_kernel + multi_merge_kernel)"
     if w.kind == "mla":
@@ -171,6 +185,8 @@ def main():
                     help="write 512 MiB of scratch before every step (outside the call's events)")
     ap.add_argument("--append-fp8", action="store_true",
                     help="FP8 workloads: append the new rows as bf16 through the quantizing append")
+    ap.add_argument("--cascade", action="store_true",
+                    help="shared-prefix workloads: attend through pkv_paged_decode_attn_cascade")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step's append and attention call as captured graphs")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -212,10 +228,23 @@ def main():
     ks, vs = put(w.k_scale), put(w.v_scale)
     nk, nv, slots = put(w.new_k), put(w.new_v), put(w.slot_mapping)
     multi = w.q_len > 1
+    cascade = bool(args.cascade)
+    if cascade and (multi or w.kind != "gqa" or not w.meta.get("prefix_blocks")):
+        sys.exit("--cascade needs a single-token GQA workload with a shared prefix")
     out = torch.empty((w.B, w.q_len, w.Hq, w.d_v) if multi else (w.B, w.Hq, w.d_v),
                       dtype=torch.float32, device=dev)
     ps = w.partition_size if args.partition is None else args.partition
-    if multi:
+    if cascade:
+        pb = w.meta["prefix_blocks"]
+        plen = pb * w.bs
+        prefix_t = put(np.ascontiguousarray(w.block_table[0, :pb]))
+        tail_np = np.ascontiguousarray(w.block_table[:, pb:])
+        tail_t = put(tail_np)
+        tail_lens_np = (w.context_lens - plen).astype(np.int32)
+        tail_l = put(tail_lens_np)
+        max_tail = int(tail_lens_np.max())
+        nbytes = pkv.cascade_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, plen, max_tail)
+    elif multi:
         nbytes = pkv.multi_workspace_bytes(w.B, w.q_len, w.Hq, w.Hkv, w.d, w.max_context_len)
     elif w.kind == "mla":
         nbytes = pkv.mla_workspace_bytes(w.B, w.Hq, w.d_v, w.max_context_len, ps)
@@ -226,7 +255,11 @@ def main():
     torch.cuda.synchronize()
 
     def attend(kp, vp):
-        if multi:
+        if cascade:
+            pkv.paged_decode_attn_cascade(out, q, kp, vp, prefix_t, plen, tail_t, tail_l, w.scale,
+                                          max_tail, kv_dtype=w.kv_dtype, k_scale=ks,
+                                          v_scale=vs, workspace=ws)
+        elif multi:
             pkv.paged_decode_attn_multi(out, q, kp, vp, bt, cl, w.scale, w.max_context_len,
                                         workspace=ws)
         elif w.kind == "mla":
@@ -309,8 +342,11 @@ def main():
         torch.cuda.synchronize()
 
     kvb = kv_bytes(w)
+    kvu = kv_unique_bytes(w)
+    shared = kvu != kvb
     call_avg = float(call_ms.mean())
-    achieved = kvb / (call_avg * 1e-3) / 1e9
+    # HBM roofline on the bytes that must come from HBM: a shared prefix once
+    achieved = kvu / (call_avg * 1e-3) / 1e9
     roofline = {
         "bound": "hbm",
         "achieved": round(achieved, 2),
@@ -366,17 +402,21 @@ def main():
             "kv_bytes_per_step": kvb, "flush_between_steps": bool(args.flush),
             "cache_copies_rotated": args.layers, "graph_replay": bool(args.graph),
             "quantizing_append": bool(append_fp8), "query_tokens_per_sequence": w.q_len,
+            "cascade": cascade,
         },
         "decode_tokens_per_s": round(w.B * w.q_len / (ms_per_step * 1e-3), 1),
         "hbm_peak_frac_step": round(kvb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {
             **roofline,
-            "traffic": traffic_for(w.name, kernel_family(w)),
-            "kernel": kernel_label(w, pkv, ps),
+            "traffic": traffic_for(w.name + ("+cascade" if cascade else ""),
+                                   "cascade" if cascade else kernel_family(w)),
+            "kernel": kernel_label(w, pkv, ps, cascade),
             "call_ms_avg": round(call_avg, 5),
             "call_ms_median": round(float(np.median(call_ms)), 5),
             "call_ms_p90": round(float(np.percentile(call_ms, 90)), 5),
-            "algorithmic_bytes_per_call": kvb,
+            "algorithmic_bytes_per_call": kvu,
+            **({"logical_bytes_per_call": kvb,
+                "logical_GBs": round(kvb / (call_avg * 1e-3) / 1e9, 2)} if shared else {}),
         },
         "cpu_baseline": None,
     }

@@ -249,7 +249,7 @@ size_t pkv_cascade_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d
  *     out[b][h] = sum_t softmax_t(scale * dot(q[b][h], K_t)) V_t over the prefix's tokens
  *                 and then sequence b's own tail tokens (KV head h / G).
  *
- * The prefix is read once per group of 64 / G sequences, with the whole group's query rows
+ * The prefix is read once per group of 32 / G sequences, with the whole group's query rows
  * as one dense product on the matrix cores, instead of once per sequence; the tails run
  * through the single-token kernel, and one merge combines both.
  *   out            [B][Hq][d] float32;  q [B][Hq][d] bfloat16

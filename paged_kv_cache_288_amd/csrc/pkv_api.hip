@@ -168,7 +168,9 @@ void multi_ws_split(void* ws, int32_t B, int32_t q_len, int32_t Hq, int32_t Hkv,
 }
 
 // Cascade call: the tail pass's balanced workspace, then the prefix pass's multi-token
-// workspace for groups of J = 64 / G sequences (64 query rows per KV head and group).
+// workspace for groups of J = 32 / G sequences (32 query rows per KV head and group: two
+// waves per SIMD; 64-row groups read the prefix half as often but take the whole register
+// file and measured slower).
 struct CascadePlan {
   bool ok;
   int32_t t_chunks, p_chunks, J, p_B;
@@ -178,11 +180,11 @@ CascadePlan cascade_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t 
                          int32_t max_tail_len) {
   CascadePlan c{false, 0, 0, 0, 0, 0, 0};
   const int32_t G = Hq / Hkv;
-  if (G < 1 || G > 64) return c;
+  if (G < 1 || G > 32) return c;
   c.t_chunks = stream_chunks(B, Hkv, max_tail_len);
   if (c.t_chunks < 0) return c;
   c.t_bytes = stream_ws_bytes(B, Hq, Hkv, d, c.t_chunks);
-  c.J = 64 / G;
+  c.J = 32 / G;
   c.p_B = (B + c.J - 1) / c.J;
   if (prefix_len > 0) {
     c.p_chunks = multi_chunks(c.p_B, c.J, Hq, Hkv, d, prefix_len);

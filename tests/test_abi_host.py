@@ -327,8 +327,8 @@ def test_cascade_rejects_bad_arguments_before_launch(lib):
 
 
 def test_cascade_workspace_size(lib):
-    """Tail pass (balanced, rows of G) then prefix pass (multi-token, 64 / G sequences per
-    group, 64 rows); 256 CUs assumed without a GPU."""
+    """Tail pass (balanced, rows of G) then prefix pass (multi-token, 32 / G sequences per
+    group, 32 rows); 256 CUs assumed without a GPU."""
     r256 = lambda x: (x + 255) // 256 * 256
     def chunks(tiles, waves):
         c = max(min(waves * 256, tiles), -(-tiles // 128))
@@ -340,9 +340,9 @@ def test_cascade_workspace_size(lib):
         rows = (ct + Hkv * B) * G
         want = 2 * r256(rows * 4) + r256(rows * d * 4) + r256((B + 1) * 4) + r256(Hkv * B * 8)
         if plen:
-            J = 64 // G
+            J = 32 // G
             pB = -(-B // J)
-            cp = chunks(Hkv * pB * -(-plen // 16), 4 if d * 4 > 256 else 8)
-            prow = (cp + Hkv * pB) * 64
+            cp = chunks(Hkv * pB * -(-plen // 16), 8)
+            prow = (cp + Hkv * pB) * 32
             want += 2 * r256(prow * 4) + r256(prow * d * 4) + r256((pB + 1) * 4) + r256(Hkv * pB * 8)
         assert lib.pkv_cascade_workspace_bytes(B, Hq, Hkv, d, plen, tmax) == want, (B, Hq)

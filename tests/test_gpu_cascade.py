@@ -3,7 +3,7 @@ against the fp64 oracle, which attends over each sequence's whole block table (p
 blocks followed by the tail blocks): the cascade must give the plain result.
 
 Covered: the FP8 shared-prefix workload reduced and at full size (sampled), bf16, every
-group size the kernels take (the prefix pass then packs 64 / G sequences per row group,
+group size the kernels take (the prefix pass then packs 32 / G sequences per row group,
 including a ragged last group), head dim 64, no prefix at all, empty tails, and a prefix
 that is the whole context."""
 
@@ -58,7 +58,7 @@ def test_cascade_fp8_prefix_reduced(seed):
 @pytest.mark.parametrize("heads", [(8, 8), (16, 8), (32, 8), (64, 8), (4, 1)])
 def test_cascade_group_sizes_bf16(heads):
     """bf16 K/V (the FP8 workload's structure with bf16 storage); group sizes 1..8, so the
-    prefix pass packs 64, 32, 16 or 8 sequences per row group (B = 37: a ragged group)."""
+    prefix pass packs 32, 16, 8 or 4 sequences per row group (B = 37: a ragged group)."""
     torch = torch_cuda()
     w = make_workload("gqa70b", seed=3, B=37, lens=("prefix", 320, 1, 400), heads=heads)
     assert w.meta["prefix_blocks"] == 20
