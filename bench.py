@@ -3,18 +3,22 @@
 A step is the whole hot path over one batch: append each sequence's newest K/V row
 (pkv_kv_append), then paged decode attention over every cached token
 (pkv_paged_decode_attn: the decode kernel and, for split contexts, the partition merge).
-Inputs are seeded synthetic tensors already resident in HBM when timing starts.
+The latent workload calls pkv_paged_decode_attn_mla, the verify workload (several query
+tokens per sequence, each appended) pkv_paged_decode_attn_multi, and --cascade on the
+shared-prefix workload pkv_paged_decode_attn_cascade.  Inputs are seeded synthetic
+tensors already resident in HBM when timing starts.
 
 Steps rotate over --layers independent copies of the KV cache (one per layer, as in a
 real model), so the 256 MB last-level cache cannot carry one step's KV into the next.
 
 Prints one JSON line.  `value` is KV GB/s for the whole step (algorithmic KV bytes read
-per step / step time); decode tokens/s is reported beside it.  `roofline` covers the
-attention call (decode + merge kernels of one pkv_paged_decode_attn call), timed with HIP
-events on the stream the library launches on.  `cpu_baseline` is the fp64 oracle timed
+per step / step time); decode tokens/s (query tokens per second) is reported beside it.
+`roofline` covers the attention call (decode + merge kernels of one call), timed with HIP
+events on the stream the library launches on; a shared prefix is counted once there.  `cpu_baseline` is the fp64 oracle timed
 on a bounded sample of the same workload on this host.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--flush]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--cascade] [--graph] [--no-cpu]
+                  [--flush]
 """
 
 import argparse

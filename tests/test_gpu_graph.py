@@ -139,3 +139,71 @@ def test_graph_begin_rejects_default_stream():
     with torch.cuda.stream(torch.cuda.default_stream()):
         with pytest.raises(pkv.PkvError):
             pkv.graph_begin()
+
+
+@pytest.mark.gpu
+def test_multi_and_cascade_calls_replay_bitwise():
+    """The multi-token and cascade calls record kernel launches only, so a captured graph
+    of both replays them exactly: every replay (with eager work and synchronisations in
+    between, and the inputs changed in place before the later ones) equals the eager calls
+    bit for bit."""
+    torch = torch_cuda()
+    import paged_kv_cache_288_amd as pkv
+    from paged_kv_cache_288_amd.workloads import to_bf16_bits
+    dev = "cuda"
+    wm = make_workload("gqa70b", seed=31, B=6, lens=("uniform", 20, 900), q_len=4)
+    wc = make_workload("fp8prefix", seed=31, B=12, lens=("prefix", 256, 0, 400))
+    qm = bits_to_device(torch, wm.q)
+    kpm, vpm = bits_to_device(torch, wm.k_pool), bits_to_device(torch, wm.v_pool)
+    btm, clm = torch.from_numpy(wm.block_table).to(dev), torch.from_numpy(wm.context_lens).to(dev)
+    pb = wc.meta["prefix_blocks"]
+    qc = bits_to_device(torch, wc.q)
+    kpc, vpc = bits_to_device(torch, wc.k_pool), bits_to_device(torch, wc.v_pool)
+    ksc, vsc = torch.from_numpy(wc.k_scale).to(dev), torch.from_numpy(wc.v_scale).to(dev)
+    prefix = torch.from_numpy(np.ascontiguousarray(wc.block_table[0, :pb])).to(dev)
+    tail_t = torch.from_numpy(np.ascontiguousarray(wc.block_table[:, pb:])).to(dev)
+    tail_np = (wc.context_lens - pb * wc.bs).astype(np.int32)
+    tail_l = torch.from_numpy(tail_np).to(dev)
+    max_tail = int(tail_np.max())
+    out_m = torch.empty((wm.B, 4, wm.Hq, wm.d), dtype=torch.float32, device=dev)
+    out_c = torch.empty((wc.B, wc.Hq, wc.d), dtype=torch.float32, device=dev)
+    ws_m = torch.empty(pkv.multi_workspace_bytes(wm.B, 4, wm.Hq, wm.Hkv, wm.d, wm.max_context_len),
+                       dtype=torch.uint8, device=dev)
+    ws_c = torch.empty(pkv.cascade_workspace_bytes(wc.B, wc.Hq, wc.Hkv, wc.d, pb * wc.bs, max_tail),
+                       dtype=torch.uint8, device=dev)
+
+    def calls():
+        pkv.paged_decode_attn_multi(out_m, qm, kpm, vpm, btm, clm, wm.scale, wm.max_context_len,
+                                    workspace=ws_m)
+        pkv.paged_decode_attn_cascade(out_c, qc, kpc, vpc, prefix, pb * wc.bs, tail_t, tail_l,
+                                      wc.scale, max_tail, kv_dtype="fp8", k_scale=ksc,
+                                      v_scale=vsc, workspace=ws_c)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pkv.graph_begin()
+        calls()
+        graph = pkv.graph_end()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4)
+    try:
+        for r in range(3):
+            if r:   # new queries in place: the graph reads the same buffers
+                qm.copy_(bits_to_device(torch, to_bf16_bits(rng.standard_normal(wm.q.shape,
+                                                                                dtype=np.float32))))
+                qc.copy_(bits_to_device(torch, to_bf16_bits(rng.standard_normal(wc.q.shape,
+                                                                                dtype=np.float32))))
+            calls()
+            torch.cuda.synchronize()
+            em, ec = out_m.clone(), out_c.clone()
+            out_m.fill_(float("nan"))
+            out_c.fill_(float("nan"))
+            graph.launch()
+            torch.cuda.synchronize()
+            assert torch.equal(out_m, em) and torch.equal(out_c, ec), f"replay {r} differs"
+            assert torch.isfinite(em).all() and torch.isfinite(ec).all()
+            log(f"[graph] multi + cascade replay {r}: bitwise equal to eager")
+    finally:
+        graph.destroy()
