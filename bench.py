@@ -26,6 +26,7 @@ import hashlib
 import json
 import os
 import re
+import subprocess
 import sys
 import time
 
@@ -128,6 +129,25 @@ def kernel_label(w, pkv, ps, cascade=False):
     return "pkv_paged_decode_attn call, partitioned (gqa_decode_kernel + partition_merge_kernel)"
 
 
+def read_ceiling():
+    """Achievable read bandwidth on this GPU, measured in the same run by the library's
+    streaming-read probe (a child process, started before this process touches the GPU):
+    the best scattered 4 KiB-chunk and grid-stride rates with nontemporal loads."""
+    exe = os.path.join(ROOT, "paged_kv_cache_288_amd", "read_ceiling")
+    if not os.path.exists(exe):
+        return None
+    try:
+        r = subprocess.run([exe], capture_output=True, text=True, timeout=180)
+    except (OSError, subprocess.TimeoutExpired):
+        return None
+    chunk = [float(m) for m in re.findall(r"scattered 4 KiB chunks, loads=nontemporal.*: ([0-9.]+) GB/s", r.stdout)]
+    stream = [float(m) for m in re.findall(r"^loads=nontemporal.*: ([0-9.]+) GB/s", r.stdout, re.M)]
+    if r.returncode != 0 or not chunk:
+        return None
+    return {"scattered_4KiB_nt_GBs": max(chunk), "grid_stride_nt_GBs": max(stream) if stream else None,
+            "probe": "paged_kv_cache_288_amd/read_ceiling (4 GiB buffer, constant and random data)"}
+
+
 def cpu_baseline(w, target_s=15.0):
     """Time the fp64 oracle on the first sequences of the workload (one thread)."""
     import oracle
@@ -193,6 +213,8 @@ def main():
                     help="shared-prefix workloads: attend through pkv_paged_decode_attn_cascade")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step's append and attention call as captured graphs")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-read ceiling probe run before the benchmark")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (to scale memory counters)")
     args = ap.parse_args()
@@ -210,6 +232,7 @@ def main():
     if not os.path.exists(pkv.library_path()):
         from paged_kv_cache_288_amd import build as _b
         _b.build(verbose=False)
+    ceiling = None if args.no_ceiling else read_ceiling()
     pkv.load_library()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda:0"
@@ -409,6 +432,9 @@ def main():
             "cascade": cascade,
         },
         "decode_tokens_per_s": round(w.B * w.q_len / (ms_per_step * 1e-3), 1),
+        **({"decode_tokens_per_s_80_layers_kv_attention_only_excludes_weights":
+            round(w.B * w.q_len / (ms_per_step * 1e-3) / 80, 1)}
+           if (w.kind, w.Hq, w.Hkv, w.d) == ("gqa", 64, 8, 128) else {}),
         "hbm_peak_frac_step": round(kvb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {
             **roofline,
@@ -422,8 +448,12 @@ def main():
             **({"logical_bytes_per_call": kvb,
                 "logical_GBs": round(kvb / (call_avg * 1e-3) / 1e9, 2)} if shared else {}),
         },
+        "read_ceiling": ceiling,
         "cpu_baseline": None,
     }
+    if ceiling:
+        result["roofline"]["frac_of_measured_read_ceiling"] = round(
+            achieved / ceiling["scattered_4KiB_nt_GBs"], 4)
     if not args.no_cpu:
         log("timing the oracle on a sample (one core)...")
         result["cpu_baseline"] = cpu_baseline(w)
