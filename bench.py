@@ -14,8 +14,9 @@ real model), so the 256 MB last-level cache cannot carry one step's KV into the 
 Prints one JSON line.  `value` is KV GB/s for the whole step (algorithmic KV bytes read
 per step / step time); decode tokens/s (query tokens per second) is reported beside it.
 `roofline` covers the attention call (decode + merge kernels of one call), timed with HIP
-events on the stream the library launches on; a shared prefix is counted once there.  `cpu_baseline` is the fp64 oracle timed
-on a bounded sample of the same workload on this host.
+events on the stream the library launches on; a shared prefix is counted once there.
+`cpu_baseline` is the fp64 oracle timed on a bounded sample of the same workload on this
+host.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--cascade] [--graph] [--no-cpu]
                   [--flush]
@@ -222,7 +223,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the decode path "
-                          "has no multi-GPU mode (see DESIGN.md, sharding)"}))
+                          "has no multi-GPU mode"}))
         sys.exit(2)
 
     import torch

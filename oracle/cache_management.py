@@ -14,7 +14,7 @@ Sources (cited by page title and section):
   "PagedAttention与Cache管理": physical blocks can be shared between requests, which
   is what prefix caching and copy-on-write build on.
 
-Readings taken where the pages are silent (also listed in the design doc):
+Readings taken where the pages are silent:
 
 * FP8 is OCP E4M3 with one fp32 scale per KV head (as for the decode path); the stored
   code of a value x is the E4M3 value nearest to the fp32 quotient x / scale (IEEE

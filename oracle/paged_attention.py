@@ -27,7 +27,7 @@ Sources (cited by page title and section):
   - section "优化三：KV 传输优化": KV carried as FP8 (half the FP16 bytes) and
     possibly computed on directly in low precision.
 
-Readings taken where the pages are silent (each is also listed in the design doc):
+Readings taken where the pages are silent:
 
 * query head h uses KV head h // G with G = Hq / Hkv (contiguous grouping);
 * a block's physical layout is [num_blocks][Hkv][block_size][d] (head-major
