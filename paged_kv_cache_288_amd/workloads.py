@@ -93,7 +93,11 @@ SPECS = {
         lens=("uniform", 1024, 8192), pool=("factor", 1.25), partition_size=0)),
     "gqa-splitk-b4-h64x8-d128-ctx32k": (2, dict(
         kind="gqa", B=4, Hq=64, Hkv=8, d=128, bs=16, kv_dtype="bf16", scale=1.0 / math.sqrt(128),
-        lens=("fixed", [32768] * 4), pool=("factor", 1.25), partition_size=512,
+        # split-K into 512-token partitions: the library's default (balanced) mode cuts this
+        # batch's 65,536 tiles into 2048 chunks of 32 tiles on a 256-CU MI355X, i.e. exactly
+        # 64 partitions of 512 tokens per (sequence, KV head); partition_size=512 selects
+        # the same split through the partitioned kernel
+        lens=("fixed", [32768] * 4), pool=("factor", 1.25), partition_size=0,
         key_boost=(0.01, 8.0))),
     "gqa-fp8-prefix4k-b128-h32x8-d128": (3, dict(
         kind="gqa", B=128, Hq=32, Hkv=8, d=128, bs=16, kv_dtype="fp8", scale=1.0 / math.sqrt(128),

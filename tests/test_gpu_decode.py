@@ -31,7 +31,11 @@ def test_decode_matches_oracle_reduced(name, seed):
     w = make_workload(name, seed=seed, **REDUCED[name])
     log(f"[decode] {w.name} seed={seed} B={w.B} lens={w.context_lens.tolist()[:8]}")
     got = gpu_decode(torch, w)
-    assert_close(got, oracle_decode(w), w.kv_dtype, f"{name}/{seed}")
+    ref = oracle_decode(w)
+    assert_close(got, ref, w.kv_dtype, f"{name}/{seed}")
+    if name == "splitk":   # the workload's named split, through the partitioned kernel
+        assert_close(gpu_decode(torch, w, partition_size=512), ref, w.kv_dtype,
+                     f"{name}/{seed} partition 512")
 
 
 @pytest.mark.parametrize("ps", [0, 16, 48, 64, 256, 512, 4096])
@@ -101,6 +105,17 @@ def test_decode_full_size_sampled(name, nsample):
     ref = oracle_decode(w, seqs)
     assert_close(got[seqs], ref, w.kv_dtype, f"{name} sampled {seqs}")
     # every output row is finite and a convex combination: bounded by the V range
+    assert np.isfinite(got).all()
+
+
+def test_splitk_partitioned_512_full_size_sampled():
+    """The long-context batch through the partitioned kernel with 512-token partitions
+    (64 per sequence and KV head), the split the workload names."""
+    torch = torch_cuda()
+    w = make_workload("splitk")
+    got = gpu_decode(torch, w, partition_size=512)
+    ref = oracle_decode(w, [2])
+    assert_close(got[[2]], ref, "bf16", "splitk partition 512, sequence 2")
     assert np.isfinite(got).all()
 
 
