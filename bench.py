@@ -41,14 +41,17 @@ HBM_PEAK_GBS = 8000.0                       # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0              # MI355X dense bf16 / fp16 matrix peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
-    "gqa": ["paged_kv_cache_288_amd/csrc/gqa_stream.hip", "paged_kv_cache_288_amd/csrc/gqa_decode.hip",
-            "paged_kv_cache_288_amd/csrc/gqa_tile.hpp", "paged_kv_cache_288_amd/csrc/pkv_device.hpp"],
+    "gqa": ["paged_kv_cache_288_amd/csrc/gqa_stream.hip", "paged_kv_cache_288_amd/csrc/gqa_stream_body.hpp",
+            "paged_kv_cache_288_amd/csrc/gqa_decode.hip", "paged_kv_cache_288_amd/csrc/gqa_tile.hpp",
+            "paged_kv_cache_288_amd/csrc/pkv_device.hpp"],
     "mla": ["paged_kv_cache_288_amd/csrc/mla_stream.hip", "paged_kv_cache_288_amd/csrc/gqa_stream.hip",
-            "paged_kv_cache_288_amd/csrc/gqa_tile.hpp", "paged_kv_cache_288_amd/csrc/pkv_device.hpp"],
-    "multi": ["paged_kv_cache_288_amd/csrc/gqa_multi.hip", "paged_kv_cache_288_amd/csrc/gqa_tile.hpp",
-              "paged_kv_cache_288_amd/csrc/pkv_device.hpp"],
-    "cascade": ["paged_kv_cache_288_amd/csrc/gqa_stream.hip", "paged_kv_cache_288_amd/csrc/gqa_multi.hip",
-                "paged_kv_cache_288_amd/csrc/gqa_tile.hpp", "paged_kv_cache_288_amd/csrc/pkv_device.hpp"],
+            "paged_kv_cache_288_amd/csrc/gqa_stream_body.hpp", "paged_kv_cache_288_amd/csrc/gqa_tile.hpp",
+            "paged_kv_cache_288_amd/csrc/pkv_device.hpp"],
+    "multi": ["paged_kv_cache_288_amd/csrc/gqa_multi.hip", "paged_kv_cache_288_amd/csrc/gqa_multi_body.hpp",
+              "paged_kv_cache_288_amd/csrc/gqa_tile.hpp", "paged_kv_cache_288_amd/csrc/pkv_device.hpp"],
+    "cascade": ["paged_kv_cache_288_amd/csrc/gqa_cascade.hip", "paged_kv_cache_288_amd/csrc/gqa_stream_body.hpp",
+                "paged_kv_cache_288_amd/csrc/gqa_multi_body.hpp", "paged_kv_cache_288_amd/csrc/gqa_tile.hpp",
+                "paged_kv_cache_288_amd/csrc/pkv_device.hpp"],
 }
 
 
@@ -115,8 +118,8 @@ def kernel_family(w):
 
 def kernel_label(w, pkv, ps, cascade=False):
     if cascade:
-        return ("pkv_paged_decode_attn_cascade call (gqa_stream_kernel over the tails, "
-                "gqa_multi_kernel over the shared prefix, cascade_merge_kernel)")
+        return ("pkv_paged_decode_attn_cascade call (cascade_kernel: tails and shared prefix "
+                "in one launch, then cascade_merge_kernel)")
     if w.q_len > 1:
         return "pkv_paged_decode_attn_multi call (gqa_multi_kernel + multi_merge_kernel)"
     if w.kind == "mla":

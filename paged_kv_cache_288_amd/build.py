@@ -19,7 +19,7 @@ LDS_PROBE = os.path.join(HERE, "lds_probe")         # standalone LDS bank probe
 ARCH = "gfx950"
 
 SOURCES = ["pkv_api.hip", "kv_append.hip", "gqa_decode.hip", "gqa_stream.hip", "mla_decode.hip",
-           "mla_stream.hip", "gqa_multi.hip"]
+           "mla_stream.hip", "gqa_multi.hip", "gqa_cascade.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -34,7 +34,8 @@ FLAGS = [
 # in AGPRs the compiler copies them around the kernel's rare rescale branch at every stage.
 # The multi-token kernel's 64-row variant needs the same to stay out of scratch.
 SOURCE_FLAGS = {"mla_stream.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-                "gqa_multi.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+                "gqa_multi.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "gqa_cascade.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src, isa):

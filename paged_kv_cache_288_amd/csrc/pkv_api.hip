@@ -170,7 +170,12 @@ void multi_ws_split(void* ws, int32_t B, int32_t q_len, int32_t Hq, int32_t Hkv,
 // Cascade call: the tail pass's balanced workspace, then the prefix pass's multi-token
 // workspace for groups of J = 32 / G sequences (32 query rows per KV head and group: two
 // waves per SIMD; 64-row groups read the prefix half as often but take the whole register
-// file and measured slower).
+// file and measured slower).  With a prefix both passes run in one launch, sized to be
+// resident together: kCascadeTailWaves + kCascadePrefixWaves waves per CU (of the splits
+// 4+4, 5+3, 6+2, 7+1, 6+1, 7+2, 8+2 and 8+4 on the FP8 shared-prefix batch, 6+2 was the
+// fastest: 69 us against 74-101 us).
+constexpr int kCascadeTailWaves = 6;
+constexpr int kCascadePrefixWaves = 2;
 struct CascadePlan {
   bool ok;
   int32_t t_chunks, p_chunks, J, p_B;
@@ -181,13 +186,13 @@ CascadePlan cascade_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t 
   CascadePlan c{false, 0, 0, 0, 0, 0, 0};
   const int32_t G = Hq / Hkv;
   if (G < 1 || G > 32) return c;
-  c.t_chunks = stream_chunks(B, Hkv, max_tail_len);
+  c.t_chunks = stream_chunks(B, Hkv, max_tail_len, prefix_len > 0 ? kCascadeTailWaves : 8);
   if (c.t_chunks < 0) return c;
   c.t_bytes = stream_ws_bytes(B, Hq, Hkv, d, c.t_chunks);
   c.J = 32 / G;
   c.p_B = (B + c.J - 1) / c.J;
   if (prefix_len > 0) {
-    c.p_chunks = multi_chunks(c.p_B, c.J, Hq, Hkv, d, prefix_len);
+    c.p_chunks = stream_chunks(c.p_B, Hkv, prefix_len, kCascadePrefixWaves);
     if (c.p_chunks < 0) return c;
     c.p_bytes = multi_ws_bytes(c.p_B, c.J, Hq, Hkv, d, c.p_chunks);
   }
@@ -510,13 +515,13 @@ pkv_status pkv_paged_decode_attn_cascade(float* out, const void* q, const void* 
                      k_scale, v_scale, tail_table, tail_lens, t_m, t_l, t_o,
                      B, Hq, Hkv, d, block_size, num_blocks, max_tail_blocks, max_tail_len,
                      0, 0, scale, fp8 ? 1 : 0, c.t_chunks, t_p, t_s};
-  pkv_status st = hip_status(pkv::launch_gqa_stream_pieces(ta, s));
-  if (st != PKV_OK) return st;
-
   // prefix: groups of J sequences as the q_len rows of the multi-token kernel, all reading
-  // the prefix blocks, no causal mask
+  // the prefix blocks, no causal mask; launched together with the tails
   pkv::MultiArgs pa{};
-  if (prefix_len > 0) {
+  pkv_status st = PKV_OK;
+  if (prefix_len == 0) {
+    st = hip_status(pkv::launch_gqa_stream_pieces(ta, s));
+  } else {
     multi_ws_split(base + c.t_bytes, c.p_B, c.J, Hq, Hkv, d, c.p_chunks, pa);
     pa.out = nullptr;
     pa.q = (const uint16_t*)q;
@@ -530,9 +535,9 @@ pkv_status pkv_paged_decode_attn_cascade(float* out, const void* q, const void* 
     pa.block_size = block_size, pa.num_blocks = num_blocks;
     pa.max_blocks = prefix_len / block_size, pa.table_stride = 0, pa.fixed_len = prefix_len;
     pa.q_rows = B, pa.causal = 0, pa.fp8 = fp8 ? 1 : 0, pa.scale = scale, pa.chunks = c.p_chunks;
-    st = hip_status(pkv::launch_gqa_multi_pieces(pa, s));
-    if (st != PKV_OK) return st;
+    st = hip_status(pkv::launch_cascade(ta, pa, s));
   }
+  if (st != PKV_OK) return st;
 
   pkv::CascadeMergeArgs ma{out, B, Hq, Hkv, d, t_m, t_l, t_o, t_p, t_s, c.t_chunks,
                            prefix_len > 0 ? pa.ws_m : nullptr, pa.ws_l, pa.ws_o, pa.ws_prefix,

@@ -131,8 +131,6 @@ struct MultiArgs {
 };
 // Decode kernel + merge kernel.
 hipError_t launch_gqa_multi(const MultiArgs& a, hipStream_t s);
-// Decode kernel only: pieces, tile prefix and segment ranges in the workspace.
-hipError_t launch_gqa_multi_pieces(const MultiArgs& a, hipStream_t s);
 // Resident waves per CU of the multi-token decode kernel for head dim d and q_len * G rows.
 int multi_waves_per_cu(int d, int rows);
 
@@ -153,5 +151,8 @@ struct CascadeMergeArgs {
   int32_t p_chunks, p_B, p_J;
 };
 hipError_t launch_cascade_merge(const CascadeMergeArgs& a, hipStream_t s);
+// Tail pass (ta, single-token balanced) and prefix pass (pa, multi-token with 32 rows) of
+// the cascade in one launch: grid (ta.chunks + pa.chunks) / 4, pieces only.
+hipError_t launch_cascade(const DecodeArgs& ta, const MultiArgs& pa, hipStream_t s);
 
 }  // namespace pkv

@@ -327,7 +327,7 @@ def test_cascade_rejects_bad_arguments_before_launch(lib):
 
 
 def test_cascade_workspace_size(lib):
-    """Tail pass (balanced, rows of G) then prefix pass (multi-token, 32 / G sequences per
+    """Tail pass (balanced, rows of G) and prefix pass (multi-token, 32 / G sequences per
     group, 32 rows); 256 CUs assumed without a GPU."""
     r256 = lambda x: (x + 255) // 256 * 256
     def chunks(tiles, waves):
@@ -336,13 +336,14 @@ def test_cascade_workspace_size(lib):
     for B, Hq, Hkv, d, plen, tmax in [(128, 32, 8, 128, 4096, 2048), (37, 8, 8, 128, 320, 401),
                                       (9, 4, 1, 64, 0, 90), (5, 64, 8, 128, 512, 0)]:
         G = Hq // Hkv
-        ct = chunks(Hkv * B * -(-tmax // 16), 8)
+        # with a prefix both passes share one launch: 6 + 2 waves per CU
+        ct = chunks(Hkv * B * -(-tmax // 16), 6 if plen else 8)
         rows = (ct + Hkv * B) * G
         want = 2 * r256(rows * 4) + r256(rows * d * 4) + r256((B + 1) * 4) + r256(Hkv * B * 8)
         if plen:
             J = 32 // G
             pB = -(-B // J)
-            cp = chunks(Hkv * pB * -(-plen // 16), 8)
+            cp = chunks(Hkv * pB * -(-plen // 16), 2)
             prow = (cp + Hkv * pB) * 32
             want += 2 * r256(prow * 4) + r256(prow * d * 4) + r256((pB + 1) * 4) + r256(Hkv * pB * 8)
         assert lib.pkv_cascade_workspace_bytes(B, Hq, Hkv, d, plen, tmax) == want, (B, Hq)
