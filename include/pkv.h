@@ -278,6 +278,28 @@ pkv_status pkv_paged_decode_attn_cascade(float* out, const void* q, const void* 
                                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pkv_validate — count violations of the caller's contract on the device (a debug aid).
+ *
+ * Cites: "深入LLM推理…" section "PagedAttention与Cache管理" (a sequence's table entries name
+ * physical blocks of the pool; each new token gets its own slot).  The decode and append
+ * calls never fault on bad values but their results are then unspecified; this call finds
+ * them.  Writes four int32 counts to the device array counts[4]:
+ *   counts[0]  table entries in use (the first ceil(L / block_size) of each row, L clamped to
+ *              the table) outside [0, num_blocks)
+ *   counts[1]  context lengths outside [0, max_blocks_per_seq * block_size]
+ *   counts[2]  slots at or past num_blocks * block_size (negative slots mean "skip", legal)
+ *   counts[3]  non-negative slots already used by an earlier token of the same append
+ *              (quadratic in T: meant for checking, not for every step)
+ * block_table [B][max_blocks_per_seq], context_lens [B] int32; slot_mapping [T] int64 (may
+ * be NULL when T = 0).  Enqueued on `stream` like the other calls; counts are valid once
+ * the stream has passed the work.
+ */
+pkv_status pkv_validate(int32_t* counts, const int32_t* block_table,
+                        const int32_t* context_lens, int32_t B, int32_t max_blocks_per_seq,
+                        int32_t num_blocks, int32_t block_size, const int64_t* slot_mapping,
+                        int32_t T, void* stream);
+
+/*
  * pkv_kv_append_fp8 — quantizing append ("PD 分离下的 KV Cache", "优化三：KV 传输优化": KV
  * kept as FP8): token i's bf16 rows k_new/v_new [T][Hkv][d] are written as FP8 E4M3 (OCP
  * e4m3fn) codes into slot_mapping[i] of the FP8 pools [num_blocks][Hkv][block_size][d],

@@ -16,7 +16,7 @@ __all__ = [
     "paged_decode_attn", "mla_workspace_bytes", "paged_decode_attn_mla", "Graph",
     "graph_begin", "graph_end", "graph_launch", "graph_destroy", "kv_append_fp8",
     "kv_copy_blocks", "block_hashes", "multi_workspace_bytes", "paged_decode_attn_multi",
-    "cascade_workspace_bytes", "paged_decode_attn_cascade",
+    "cascade_workspace_bytes", "paged_decode_attn_cascade", "validate",
 ]
 
 PKV_BF16 = 1
@@ -60,6 +60,8 @@ _SIGNATURES = [
                                                  _c_int32, _c_int32, _c_int32, _c_int32,
                                                  _c_int32, _c_int32, _c_int32, _c_int32,
                                                  ctypes.c_float, _c_int32, _p, _c_size, _p]),
+    ("pkv_validate", _c_int32, [_p, _p, _p, _c_int32, _c_int32, _c_int32, _c_int32, _p, _c_int32,
+                                _p]),
     ("pkv_kv_append_fp8", _c_int32, [_p, _p, _p, _p, _p, _p, _p, _c_int32, _c_int32, _c_int32,
                                      _c_int32, _c_int32, _p]),
     ("pkv_kv_copy_blocks", _c_int32, [_p, _p, _p, _p, _c_int32, _c_int32, _c_int32, _c_int32,
@@ -256,6 +258,23 @@ def paged_decode_attn_cascade(out, q, k_pool, v_pool, prefix_blocks, prefix_len,
         _ptr(workspace), wsize, _stream(q.device))
     _check("pkv_paged_decode_attn_cascade", st)
     return out
+
+
+def validate(block_table, context_lens, num_blocks, block_size, slot_mapping=None):
+    """Count caller-contract violations on the device (pkv_validate): returns a dict with
+    the table entries in use outside the pool, context lengths outside the table, slots
+    past the pool and slots written twice.  Synchronises the current stream."""
+    import torch
+    counts = torch.empty(4, dtype=torch.int32, device=block_table.device)
+    B, mb = block_table.shape
+    T = 0 if slot_mapping is None else slot_mapping.shape[0]
+    st = load_library().pkv_validate(
+        _ptr(counts), _ptr(block_table), _ptr(context_lens), B, mb, num_blocks, block_size,
+        _ptr(slot_mapping), T, _stream(block_table.device))
+    _check("pkv_validate", st)
+    c = counts.cpu().tolist()
+    return {"bad_block_ids": c[0], "bad_context_lens": c[1], "slots_past_pool": c[2],
+            "duplicate_slots": c[3]}
 
 
 def kv_append_fp8(k_pool, v_pool, k_new, v_new, k_scale, v_scale, slot_mapping):

@@ -19,7 +19,7 @@ LDS_PROBE = os.path.join(HERE, "lds_probe")         # standalone LDS bank probe
 ARCH = "gfx950"
 
 SOURCES = ["pkv_api.hip", "kv_append.hip", "gqa_decode.hip", "gqa_stream.hip", "mla_decode.hip",
-           "mla_stream.hip", "gqa_multi.hip", "gqa_cascade.hip"]
+           "mla_stream.hip", "gqa_multi.hip", "gqa_cascade.hip", "validate.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

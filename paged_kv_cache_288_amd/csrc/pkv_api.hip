@@ -545,6 +545,23 @@ pkv_status pkv_paged_decode_attn_cascade(float* out, const void* q, const void* 
   return hip_status(pkv::launch_cascade_merge(ma, s));
 }
 
+pkv_status pkv_validate(int32_t* counts, const int32_t* block_table,
+                        const int32_t* context_lens, int32_t B, int32_t max_blocks_per_seq,
+                        int32_t num_blocks, int32_t block_size, const int64_t* slot_mapping,
+                        int32_t T, void* stream) {
+  if (B < 0 || T < 0 || num_blocks <= 0 || block_size <= 0 || max_blocks_per_seq < 0)
+    return PKV_ERR_SHAPE;
+  if (!counts || (B > 0 && max_blocks_per_seq > 0 && (!block_table || !context_lens)) ||
+      (T > 0 && !slot_mapping))
+    return PKV_ERR_NULL;
+  if (!aligned4(counts) || (B > 0 && (!aligned4(block_table) || !aligned4(context_lens))) ||
+      ((uintptr_t)slot_mapping & 7u))
+    return PKV_ERR_ALIGN;
+  pkv::ValidateArgs a{counts, block_table, context_lens, B, max_blocks_per_seq, num_blocks,
+                      block_size, slot_mapping, T};
+  return hip_status(pkv::launch_validate(a, (hipStream_t)stream));
+}
+
 pkv_status pkv_kv_append_fp8(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                              const float* k_scale, const float* v_scale,
                              const int64_t* slot_mapping, int32_t T, int32_t num_blocks,

@@ -100,6 +100,17 @@ hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t s);
 int mla_stream_heads_per_group(int Hq);
 hipError_t launch_mla_stream(const MlaArgs& a, hipStream_t s);
 
+// Debug check of block tables, context lengths and append slots (counts into counts[4]).
+struct ValidateArgs {
+  int32_t* counts;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  int32_t B, max_blocks, num_blocks, block_size;
+  const int64_t* slots;  // may be null
+  int32_t T;
+};
+hipError_t launch_validate(const ValidateArgs& a, hipStream_t s);
+
 // Multi-token decode (q_len query tokens per sequence, causal among them), balanced mode
 // only.  Row n of segment (g, b) is query token n / G, head g * G + n % G.  The same kernel
 // serves the shared-prefix pass of the cascade call: there the "sequences" are groups of

@@ -347,3 +347,22 @@ def test_cascade_workspace_size(lib):
             prow = (cp + Hkv * pB) * 32
             want += 2 * r256(prow * 4) + r256(prow * d * 4) + r256((pB + 1) * 4) + r256(Hkv * pB * 8)
         assert lib.pkv_cascade_workspace_bytes(B, Hq, Hkv, d, plen, tmax) == want, (B, Hq)
+
+
+def test_validate_rejects_bad_arguments_before_launch(lib):
+    f = lib.pkv_validate
+    # counts table lens B mb nb bs slots T stream
+    base = [FAKE, FAKE, FAKE, 4, 8, 100, 16, FAKE, 10, None]
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a3=-1) == -2
+    assert call(a5=0) == -2
+    assert call(a6=0) == -2
+    assert call(a0=None) == -1
+    assert call(a1=None) == -1
+    assert call(a7=None) == -1           # T > 0 needs slots
+    assert call(a0=ctypes.c_void_p(0x1002)) == -5   # counts must be 4-byte aligned
+    assert call(a7=ctypes.c_void_p(0x1004)) == -5   # slots must be 8-byte aligned
