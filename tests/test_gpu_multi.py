@@ -144,3 +144,27 @@ def test_multi_rejects_unsupported():
     with pytest.raises(pkv.PkvError) as e:
         gpu_multi(torch, w)
     assert e.value.status == pkv.PKV_ERR_UNSUPPORTED
+
+
+def test_multi_block_size_64():
+    """64-token blocks (four 16-token tiles per block): the same histories re-blocked."""
+    torch = torch_cuda()
+    w = make_workload("gqa70b", seed=12, B=3, lens=("uniform", 5, 700), q_len=3)
+    ref = oracle_multi(w)
+    bs, L = 64, w.context_lens
+    nb = int(sum(-(-int(x) // bs) for x in L)) + 2
+    perm = np.random.default_rng(64).permutation(nb)
+    kp = np.full((nb, w.Hkv, bs, w.d), 0x7FC0, np.uint16)
+    vp = kp.copy()
+    table = np.full((w.B, -(-int(L.max()) // bs)), -1, np.int32)
+    cur = 0
+    for b in range(w.B):
+        n = -(-int(L[b]) // bs)
+        table[b, :n] = perm[cur:cur + n]
+        cur += n
+        for t in range(int(L[b])):
+            pb, off = w.block_table[b, t // 16], t % 16
+            kp[table[b, t // bs], :, t % bs] = w.k_pool[pb, :, off]
+            vp[table[b, t // bs], :, t % bs] = w.v_pool[pb, :, off]
+    w.k_pool, w.v_pool, w.block_table, w.bs = kp, vp, table, bs
+    assert_close(gpu_multi(torch, w), ref, "bf16", "multi block size 64")
