@@ -216,7 +216,7 @@ size_t pkv_multi_workspace_bytes(int32_t B, int32_t q_len, int32_t Hq, int32_t H
  *   max_context_len, workspace: as for pkv_paged_decode_attn (the workspace size from
  *   pkv_multi_workspace_bytes).
  * Supported: bf16 or FP8 K/V, d in {64, 128}, block_size a multiple of 16,
- * (Hq / Hkv) * q_len <= 64, B <= 4096.  Precision: scores on the bf16 MFMA (FP8 codes
+ * Hq / Hkv in {1, 2, 4, 8}, (Hq / Hkv) * q_len <= 64, B <= 4096.  Precision: scores on the bf16 MFMA (FP8 codes
  * widened exactly to bf16), weights and V in fp16 on the fp16 MFMA (fp32 accumulate), so
  * |v| < 65504 as for the latent call.
  */

@@ -42,28 +42,37 @@ __global__ __launch_bounds__(kMW * kWave, multi_waves_per_simd(D, RT)) void gqa_
   gqa_multi_body<D, RT, FP8>(a, blockIdx.x, s_pre, s_sum, s_v);
 }
 
-// out[b][j][hq] = merge of the pieces of segment (g = hq / G, b), row j * G + hq % G.
-// One wave per output row, kMergeWaves per workgroup.
+// out[b][j][g*G .. g*G + G) = merge of the pieces of segment (g, b), rows j*G .. j*G + G.
+// One wave per (sequence, query token, KV head): the G rows are contiguous both in every
+// piece slot and in the output, so each piece is one G*D-float run read by the whole wave
+// (float4 per lane), and the output one run written by it.  Piece weights: lane q*G + h
+// holds piece p0 + q, row h, for 64/G pieces per pass.
 constexpr int kMultiMergeWaves = 4;
-template <int D>
+template <int D, int G>
 __global__ __launch_bounds__(kMultiMergeWaves * kWave) void multi_merge_kernel(MultiArgs a) {
-  constexpr int PER = D / kWave;
-  const int G = a.Hq / a.Hkv, R = G * a.q_len;
-  const int idx = blockIdx.x * kMultiMergeWaves + (int)(threadIdx.x / kWave);
-  if (idx >= a.B * a.q_len * a.Hq) return;
-  const int b = idx / (a.q_len * a.Hq), rem = idx - b * (a.q_len * a.Hq);
-  const int jq = rem / a.Hq, hq = rem - jq * a.Hq, g = hq / G, row = jq * G + (hq - g * G);
+  constexpr int RUN = G * D;                      // floats per piece run
+  constexpr int NF4 = RUN >= 4 * kWave ? RUN / (4 * kWave) : 1;  // float4 per lane per run
+  constexpr int ACTIVE = RUN >= 4 * kWave ? kWave : RUN / 4;     // lanes holding data
+  constexpr int PP = kWave / G;                   // pieces per weight pass
+  constexpr int U = PP < 8 ? PP : 8;              // pieces whose loads are in flight together
+  const int R = G * a.q_len;
+  const int wv = blockIdx.x * kMultiMergeWaves + (int)(threadIdx.x / kWave);
+  if (wv >= a.B * a.q_len * a.Hkv) return;
+  const int g = wv % a.Hkv, bj = wv / a.Hkv, b = bj / a.q_len, jq = bj - b * a.q_len;
   const int lane = threadIdx.x & (kWave - 1);
-  float* out = a.out + (size_t)idx * D;
+  const int hw = lane % G, qw = lane / G;         // weight lane: row hw of piece p0 + qw
+  float* out = a.out + ((size_t)bj * a.Hq + (size_t)g * G) * D;
   const int c0 = a.ws_seg[2 * (g * a.B + b)], np = a.ws_seg[2 * (g * a.B + b) + 1];
-  const int T_head = a.ws_prefix[a.B];
   if (np == 0) {
+    if (lane < ACTIVE)
 #pragma unroll
-    for (int i = 0; i < PER; ++i) out[lane + kWave * i] = 0.f;
+      for (int k = 0; k < NF4; ++k)
+        *(float4*)(out + 4 * (lane + kWave * k)) = make_float4(0.f, 0.f, 0.f, 0.f);
     return;
   }
-  const long long T = (long long)a.Hkv * T_head;
+  const long long T = (long long)a.Hkv * a.ws_prefix[a.B];
   const size_t slot0 = (size_t)c0 + (size_t)g * a.B + b;  // slot of piece i: slot0 + i
+  const size_t row0 = (size_t)jq * G;
   // with fewer tiles than chunks some chunks are empty and wrote nothing
   const bool all_live = T >= a.chunks;
   auto live = [&](int i) {
@@ -71,30 +80,78 @@ __global__ __launch_bounds__(kMultiMergeWaves * kWave) void multi_merge_kernel(M
     const long long cc = c0 + i;
     return T * cc / a.chunks != T * (cc + 1) / a.chunks;
   };
-  float M = kNegInf;
-  for (int p0 = 0; p0 < np; p0 += kWave)
-    if (p0 + lane < np && live(p0 + lane)) M = fmaxf(M, a.ws_m[(slot0 + p0 + lane) * R + row]);
+  // reduce over the lanes of one row (lane bits above log2 G)
+  auto row_max = [](float x) {
 #pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) M = fmaxf(M, __shfl_xor(M, s));
-  RowAcc<D> acc;
-  rows_clear(acc);
+    for (int s = G; s < kWave; s <<= 1) x = fmaxf(x, __shfl_xor(x, s));
+    return x;
+  };
+  auto row_sum = [](float x) {
+#pragma unroll
+    for (int s = G; s < kWave; s <<= 1) x += __shfl_xor(x, s);
+    return x;
+  };
+  float M = kNegInf;
+  for (int p0 = 0; p0 < np; p0 += PP)
+    if (p0 + qw < np && live(p0 + qw)) M = fmaxf(M, a.ws_m[(slot0 + p0 + qw) * R + row0 + hw]);
+  M = row_max(M);
+
+  // data lanes: float4 k of a run covers row (4 lane + 4 kWave k) / D
+  float4 acc[NF4];
+#pragma unroll
+  for (int k = 0; k < NF4; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
   float den = 0.f;
-  for (int p0 = 0; p0 < np; p0 += kWave) {
+  for (int p0 = 0; p0 < np; p0 += PP) {
     float f = 0.f, lp = 0.f;
-    if (p0 + lane < np && live(p0 + lane)) {
-      const size_t si = (slot0 + p0 + lane) * R + row;
+    if (p0 + qw < np && live(p0 + qw)) {
+      const size_t si = (slot0 + p0 + qw) * R + row0 + hw;
       const float mp = a.ws_m[si];
       lp = a.ws_l[si];
       f = (mp == kNegInf) ? 0.f : fast_exp2(mp - M);
     }
-    float fl = f * lp;
+    den += row_sum(f * lp);
+    const int cnt = min(PP, np - p0);
+    // U pieces' loads issued together, then their products
+    for (int q0 = 0; q0 < cnt; q0 += U) {
+      float fk[U][NF4];
+      float4 x[U][NF4];
 #pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) fl += __shfl_xor(fl, s);
-    den += fl;
-    rows_accumulate<D>(acc, a.ws_o + ((slot0 + p0) * R + row) * D, (size_t)R * D, f,
-                       min(kWave, np - p0), lane);
+      for (int u = 0; u < U; ++u) {
+        const int q = q0 + u;
+        const float* run = a.ws_o + ((slot0 + p0 + (q < cnt ? q : 0)) * R + row0) * D;
+#pragma unroll
+        for (int k = 0; k < NF4; ++k) {
+          const int e = 4 * (lane + kWave * k);
+          fk[u][k] = __shfl(f, (q < cnt ? q : 0) * G + (e / D) % G);
+          if (q >= cnt) fk[u][k] = 0.f;
+          x[u][k] = (lane < ACTIVE && fk[u][k] != 0.f) ? *(const float4*)(run + e)
+                                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int k = 0; k < NF4; ++k) {
+          acc[k].x += fk[u][k] * x[u][k].x;
+          acc[k].y += fk[u][k] * x[u][k].y;
+          acc[k].z += fk[u][k] * x[u][k].z;
+          acc[k].w += fk[u][k] * x[u][k].w;
+        }
+    }
   }
-  rows_store<D>(acc, out, den > 0.f ? 1.f / den : 0.f, lane);
+  // the row sums, from the lanes that hold them, in every lane (all lanes shuffle)
+  float sc[NF4];
+#pragma unroll
+  for (int k = 0; k < NF4; ++k) {
+    const float d = __shfl(den, (4 * (lane + kWave * k) / D) % G);
+    sc[k] = d > 0.f ? 1.f / d : 0.f;
+  }
+  if (lane < ACTIVE) {
+#pragma unroll
+    for (int k = 0; k < NF4; ++k)
+      *(float4*)(out + 4 * (lane + kWave * k)) =
+          make_float4(acc[k].x * sc[k], acc[k].y * sc[k], acc[k].z * sc[k], acc[k].w * sc[k]);
+  }
 }
 
 template <int D, int RT, bool FP8>
@@ -102,8 +159,15 @@ static hipError_t launch_multi_one(const MultiArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((gqa_multi_kernel<D, RT, FP8>), dim3(a.chunks / kMW), dim3(kMW * kWave), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)(((long long)a.B * a.q_len * a.Hq + kMultiMergeWaves - 1) / kMultiMergeWaves));
-  hipLaunchKernelGGL(multi_merge_kernel<D>, grid, dim3(kMultiMergeWaves * kWave), 0, s, a);
+  const dim3 grid((unsigned)(((long long)a.B * a.q_len * a.Hkv + kMultiMergeWaves - 1) / kMultiMergeWaves));
+  const dim3 block(kMultiMergeWaves * kWave);
+  switch (a.Hq / a.Hkv) {
+    case 1: hipLaunchKernelGGL((multi_merge_kernel<D, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((multi_merge_kernel<D, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((multi_merge_kernel<D, 4>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((multi_merge_kernel<D, 8>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -411,7 +411,10 @@ pkv_status pkv_paged_decode_attn_mla(float* out, const void* q, const void* kv_p
 size_t pkv_multi_workspace_bytes(int32_t B, int32_t q_len, int32_t Hq, int32_t Hkv, int32_t d,
                                  int32_t max_context_len) {
   if (!multi_shape_ok(B, q_len, Hq, Hkv, d, max_context_len)) return 0;
-  if ((long long)(Hq / Hkv) * q_len > 64 || (long long)Hkv * B >= (1LL << 26)) return 0;
+  const int32_t G = Hq / Hkv;
+  if ((long long)G * q_len > 64 || (G != 1 && G != 2 && G != 4 && G != 8) ||
+      (long long)Hkv * B >= (1LL << 26))
+    return 0;
   const int32_t chunks = multi_chunks(B, q_len, Hq, Hkv, d, max_context_len);
   return chunks < 0 ? 0 : multi_ws_bytes(B, q_len, Hq, Hkv, d, chunks);
 }
@@ -432,7 +435,9 @@ pkv_status pkv_paged_decode_attn_multi(float* out, const void* q, const void* k_
   if (!out || !q || !k_pool || !v_pool || !block_table || !context_lens) return PKV_ERR_NULL;
   const bool fp8 = kv_dtype == PKV_FP8_E4M3;
   if (fp8 && (!k_scale || !v_scale)) return PKV_ERR_NULL;
-  if ((d != 128 && d != 64) || block_size % 16 || (long long)(Hq / Hkv) * q_len > 64)
+  const int32_t G = Hq / Hkv;
+  if ((d != 128 && d != 64) || block_size % 16 || (long long)G * q_len > 64 ||
+      (G != 1 && G != 2 && G != 4 && G != 8))
     return PKV_ERR_UNSUPPORTED;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
       !aligned4(block_table) || !aligned4(context_lens) ||

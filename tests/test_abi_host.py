@@ -277,6 +277,7 @@ def test_multi_rejects_bad_arguments_before_launch(lib):
     assert call(a0=None) == -1
     assert call(a18=pkv.PKV_FP8_E4M3) == -1   # FP8 needs its scales
     assert call(a9=9) == -4              # 72 rows per KV head
+    assert call(a10=48) == -4            # group of 6 query heads
     assert call(a12=96) == -4
     assert call(a13=8) == -4
     assert call(a1=MIS) == -5
