@@ -103,7 +103,85 @@ static hipError_t launch_stream_d(const DecodeArgs& a, hipStream_t s, bool merge
   }
 }
 
+// The same merge for segments of many pieces (a few long contexts): one workgroup per
+// output row, its four waves each taking a contiguous quarter of the pieces; the quarter
+// maxima, then the weighted sums, are combined through LDS.  Spreads the latency-bound
+// chain of loads over four waves when there are too few rows to fill the GPU.
+template <int D>
+__global__ __launch_bounds__(kMergeWaves * kWave) void stream_merge_long_kernel(DecodeArgs a) {
+  constexpr int PER = D / kWave;
+  __shared__ float s_m[kMergeWaves], s_den[kMergeWaves];
+  __shared__ __attribute__((aligned(16))) float s_acc[kMergeWaves][D];
+  const int G = a.Hq / a.Hkv;
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hq, hq = bh - b * a.Hq, g = hq / G, h = hq - g * G;
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  float* out = a.out + (size_t)bh * D;
+  const int c0 = a.ws_seg[2 * (g * a.B + b)], np = a.ws_seg[2 * (g * a.B + b) + 1];
+  if (np == 0) {  // workgroup-uniform
+    if (w == 0)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) out[lane + kWave * i] = 0.f;
+    return;
+  }
+  const long long T = (long long)a.Hkv * a.ws_prefix[a.B];
+  const size_t slot0 = (size_t)c0 + (size_t)g * a.B + b;
+  const bool all_live = T >= a.chunks;
+  auto live = [&](int i) {
+    if (all_live) return true;
+    const long long cc = c0 + i;
+    return T * cc / a.chunks != T * (cc + 1) / a.chunks;
+  };
+  const int lo = (int)((long long)np * w / kMergeWaves), hi = (int)((long long)np * (w + 1) / kMergeWaves);
+  float M = kNegInf;
+  for (int p0 = lo; p0 < hi; p0 += kWave)
+    if (p0 + lane < hi && live(p0 + lane)) M = fmaxf(M, a.ws_m[(slot0 + p0 + lane) * G + h]);
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) M = fmaxf(M, __shfl_xor(M, s));
+  if (lane == 0) s_m[w] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  RowAcc<D> acc;
+  rows_clear(acc);
+  float den = 0.f;
+  for (int p0 = lo; p0 < hi; p0 += kWave) {
+    float f = 0.f, lp = 0.f;
+    if (p0 + lane < hi && live(p0 + lane)) {
+      const size_t si = (slot0 + p0 + lane) * G + h;
+      const float mp = a.ws_m[si];
+      lp = a.ws_l[si];
+      f = (mp == kNegInf) ? 0.f : fast_exp2(mp - M);
+    }
+    float fl = f * lp;
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) fl += __shfl_xor(fl, s);
+    den += fl;
+    rows_accumulate<D>(acc, a.ws_o + ((slot0 + p0) * G + h) * D, (size_t)G * D, f,
+                       min(kWave, hi - p0), lane);
+  }
+  // this wave's weighted sum (scale 1) into LDS, then wave 0 adds the four
+  rows_store<D>(acc, s_acc[w], 1.f, lane);
+  if (lane == 0) s_den[w] = den;
+  __syncthreads();
+  if (w == 0) {
+    const float d = s_den[0] + s_den[1] + s_den[2] + s_den[3];
+    const float sc = d > 0.f ? 1.f / d : 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = lane + kWave * i;
+      out[e] = (s_acc[0][e] + s_acc[1][e] + s_acc[2][e] + s_acc[3][e]) * sc;
+    }
+  }
+}
+
 hipError_t launch_stream_merge(const DecodeArgs& a, hipStream_t s) {
+  const long long segs = (long long)a.Hkv * a.B;
+  if ((a.d == 128 || a.d == 64) && a.chunks + segs > 16 * segs) {
+    const dim3 grid((unsigned)(a.B * a.Hq)), block(kMergeWaves * kWave);
+    if (a.d == 128) hipLaunchKernelGGL(stream_merge_long_kernel<128>, grid, block, 0, s, a);
+    else hipLaunchKernelGGL(stream_merge_long_kernel<64>, grid, block, 0, s, a);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((a.B * a.Hq + kMergeWaves - 1) / kMergeWaves)), block(kMergeWaves * kWave);
   if (a.d == 128) hipLaunchKernelGGL(stream_merge_kernel<128>, grid, block, 0, s, a);
   else if (a.d == 64) hipLaunchKernelGGL(stream_merge_kernel<64>, grid, block, 0, s, a);
