@@ -440,10 +440,10 @@ def test_unmutated_namespace_passes_every_pin():
         pin(ns2)
 
 
-def test_multi_token_decode_is_causal_attention_over_the_new_tokens():
-    """Pinned against dense attention with an explicit causal mask over the gathered
-    sequence (the new tokens are its last q_len positions), q_len = 1 against the
-    single-token oracle, and a token whose context is empty against 0."""
+def _pin_multi_token(multi_fn):
+    """Pin of the multi-token decode: dense attention with an explicit causal mask over
+    the gathered sequence (the new tokens are its last q_len positions), q_len = 1 against
+    the single-token oracle, and a token whose context is empty against 0."""
     rng = np.random.default_rng(21)
     B, q_len, Hq, Hkv, d, bs = 3, 4, 4, 2, 8, 4
     lens = np.array([9, 4, 2])
@@ -452,7 +452,7 @@ def test_multi_token_decode_is_causal_attention_over_the_new_tokens():
     v_pool = rng.standard_normal((nb, Hkv, bs, d))
     table = np.array([[3, 0, 6], [5, 1, 7], [2, 4, 7]])
     q = rng.standard_normal((B, q_len, Hq, d))
-    got = REAL.multi_token_decode_attention(q, k_pool, v_pool, table, lens, 0.3)
+    got = multi_fn(q, k_pool, v_pool, table, lens, 0.3)
     G = Hq // Hkv
     for b in range(B):
         L = int(lens[b])
@@ -469,6 +469,38 @@ def test_multi_token_decode_is_causal_attention_over_the_new_tokens():
                     continue
                 p = np.exp(S[j] - S[j].max())
                 assert np.allclose(got[b, j, h], p @ V[h // G] / p.sum(), rtol=1e-12, atol=1e-12)
-    one = REAL.multi_token_decode_attention(q[:, :1], k_pool, v_pool, table, lens, 0.3)
+    one = multi_fn(q[:, :1], k_pool, v_pool, table, lens, 0.3)
     assert np.array_equal(one[:, 0], REAL.paged_decode_attention(q[:, 0], k_pool, v_pool,
                                                                     table, lens, 0.3))
+
+
+def test_multi_token_decode_is_causal_attention_over_the_new_tokens():
+    _pin_multi_token(REAL.multi_token_decode_attention)
+
+
+def _multi_mutant(shift=0, reverse=False, causal=True):
+    """The multi-token oracle with one plausible mistake: the visible length off by
+    `shift`, the query tokens taken in reverse order, or no causal mask at all."""
+    def fn(q, k_pool, v_pool, block_table, context_lens, scale):
+        q = np.asarray(q, dtype=np.float64)
+        B, q_len = q.shape[:2]
+        lens = np.asarray(context_lens, dtype=np.int64)
+        out = np.zeros(q.shape[:3] + (np.asarray(v_pool).shape[-1],))
+        for j in range(q_len):
+            jj = q_len - 1 - j if reverse else j
+            seen = lens - (q_len - 1 - jj) + shift if causal else lens
+            out[:, j] = REAL.paged_decode_attention(q[:, j], k_pool, v_pool, block_table,
+                                                    np.clip(seen, 0, lens), scale)
+        return out
+    return fn
+
+
+@pytest.mark.parametrize("mutant", [dict(shift=-1), dict(shift=1), dict(reverse=True),
+                                    dict(causal=False)])
+def test_multi_token_pin_catches_planted_mistakes(mutant):
+    with pytest.raises(AssertionError):
+        _pin_multi_token(_multi_mutant(**mutant))
+
+
+def test_multi_token_mutant_without_mistake_passes():
+    _pin_multi_token(_multi_mutant())
