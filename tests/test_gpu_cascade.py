@@ -98,3 +98,15 @@ def test_cascade_full_size_sampled():
     seqs = sorted(np.random.default_rng(77).choice(w.B, size=8, replace=False).tolist())
     assert_close(got[seqs], oracle_decode(w, seqs), "fp8", f"fp8prefix cascade sampled {seqs}")
     assert np.isfinite(got).all()
+
+
+def test_cascade_edge_batches():
+    """A single sequence (one row group with 3 padding sequences at G = 8), and a batch
+    whose contexts are all empty (no prefix, zero-length tails): zeros."""
+    torch = torch_cuda()
+    w = make_workload("gqa70b", seed=17, B=1, lens=("prefix", 256, 1, 50))
+    assert_close(gpu_cascade(torch, w), oracle_decode(w), "bf16", "single sequence")
+    w = make_workload("gqa70b", seed=18, B=4, lens=("prefix", 64, 0, 40))
+    w.context_lens[:] = 0
+    got = gpu_cascade(torch, w, prefix_blocks=0)
+    assert (got == 0).all()
