@@ -110,3 +110,25 @@ def test_cascade_edge_batches():
     w.context_lens[:] = 0
     got = gpu_cascade(torch, w, prefix_blocks=0)
     assert (got == 0).all()
+
+
+def test_cascade_linearity_in_v_is_exact():
+    """V x 2 doubles the cascade's output bit for bit (prefix and tail passes alike)."""
+    torch = torch_cuda()
+    w = make_workload("gqa70b", seed=19, B=9, lens=("prefix", 128, 1, 200))
+    w.v_pool, doubled = _double_v_exactly(w.v_pool)
+    a = gpu_cascade(torch, w)
+    w.v_pool = doubled
+    b = gpu_cascade(torch, w)
+    assert np.array_equal(b, 2 * a)
+
+
+def _double_v_exactly(v_pool):
+    """V with the N(0,1) draws below 2^-14 in magnitude zeroed (p.V widens V to fp16, exact
+    only in fp16's normal range), and that V times 2 (exponent + 1, exact in bf16)."""
+    v = v_pool.view(np.uint16).copy()
+    exp = (v >> 7) & 0xFF
+    v = np.where((exp != 0xFF) & (exp < 127 - 14), np.uint16(0), v).astype(np.uint16)
+    exp = (v >> 7) & 0xFF
+    ok = (exp != 0xFF) & (exp > 0) & (exp < 0xFE)
+    return v, np.where(ok, v + np.uint16(1 << 7), v).astype(np.uint16)

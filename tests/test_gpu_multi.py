@@ -168,3 +168,26 @@ def test_multi_block_size_64():
             vp[table[b, t // bs], :, t % bs] = w.v_pool[pb, :, off]
     w.k_pool, w.v_pool, w.block_table, w.bs = kp, vp, table, bs
     assert_close(gpu_multi(torch, w), ref, "bf16", "multi block size 64")
+
+
+def test_multi_linearity_in_v_is_exact():
+    """V x 2 (exact in bf16 and in the fp16 the products use) doubles every output bit for
+    bit: the weights do not depend on V and every rounding scales by the power of two."""
+    torch = torch_cuda()
+    w = make_workload("gqa70b", seed=14, B=3, lens=("uniform", 30, 600), q_len=4)
+    w.v_pool, doubled = _double_v_exactly(w.v_pool)
+    a = gpu_multi(torch, w)
+    w.v_pool = doubled
+    b = gpu_multi(torch, w)
+    assert np.array_equal(b, 2 * a)
+
+
+def _double_v_exactly(v_pool):
+    """V with the N(0,1) draws below 2^-14 in magnitude zeroed (p.V widens V to fp16, exact
+    only in fp16's normal range), and that V times 2 (exponent + 1, exact in bf16)."""
+    v = v_pool.view(np.uint16).copy()
+    exp = (v >> 7) & 0xFF
+    v = np.where((exp != 0xFF) & (exp < 127 - 14), np.uint16(0), v).astype(np.uint16)
+    exp = (v >> 7) & 0xFF
+    ok = (exp != 0xFF) & (exp > 0) & (exp < 0xFE)
+    return v, np.where(ok, v + np.uint16(1 << 7), v).astype(np.uint16)
