@@ -16,6 +16,7 @@
 // last round.  Chunks are numbered so that each XCD (workgroup id mod 8 under round-robin
 // dispatch) gets a contiguous eighth of the space - one KV head when Hkv = 8 - so a shared
 // prefix's re-reads stay in that XCD's L2.
+#include "gqa_ring_body.hpp"
 #include "gqa_stream_body.hpp"
 
 namespace pkv {
@@ -83,10 +84,23 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void stream_merge_kernel(Decod
   rows_store<D>(acc, out, den > 0.f ? 1.f / den : 0.f, lane);
 }
 
+// The library's default single-token decode: one workgroup of kRingWaves waves per CU,
+// each wave streaming its chunk through an LDS ring (gqa_ring_body.hpp).
+template <int D, int G, bool FP8>
+__global__ __launch_bounds__(kRingWaves * kWave, 1) void gqa_ring_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t s_lds[ring_lds_bytes<D, G, FP8>()];
+  gqa_ring_body<D, G, FP8>(a, blockIdx.x, (lds_u8_t*)s_lds);
+}
+
 template <int D, int G, bool FP8>
 static hipError_t launch_stream_one(const DecodeArgs& a, hipStream_t s, bool merge) {
-  hipLaunchKernelGGL((gqa_stream_kernel<D, G, FP8>), dim3(a.chunks / kWaves), dim3(kWaves * kWave),
-                     0, s, a);
+  if (merge) {
+    hipLaunchKernelGGL((gqa_ring_kernel<D, G, FP8>), dim3(a.chunks / kRingWaves),
+                       dim3(kRingWaves * kWave), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((gqa_stream_kernel<D, G, FP8>), dim3(a.chunks / kWaves),
+                       dim3(kWaves * kWave), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !merge) return e;
   return launch_stream_merge(a, s);

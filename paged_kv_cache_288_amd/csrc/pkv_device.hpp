@@ -161,7 +161,8 @@ __device__ __forceinline__ void segment_range(long long first, int nb, long long
   out[0] = c0;
   out[1] = n;
 }
-__device__ __forceinline__ void write_segment_ranges(int32_t* ws_seg, const int* pre, int B,
+template <typename PRE>  // any pointer to int (generic or LDS)
+__device__ __forceinline__ void write_segment_ranges(int32_t* ws_seg, PRE pre, int B,
                                                      int H, int C, int tid, int nthreads) {
   const int T_head = pre[B];
   const long long T = (long long)H * T_head;
