@@ -152,6 +152,56 @@ def read_ceiling():
             "probe": "paged_kv_cache_288_amd/read_ceiling (4 GiB buffer, constant and random data)"}
 
 
+class TimingEvent:
+    """A HIP event for timing only (hipEventDisableSystemFence): recording it does not write
+    back and invalidate the caches, as an ordinary event does (the HIP documentation gives
+    this flag for events that only measure time, for more accurate timings).  Recorded on the
+    stream the library launches on (torch's current stream)."""
+
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            import ctypes
+            lib = ctypes.CDLL("libamdhip64.so")
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = lib
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._ev = ctypes.c_void_p()
+        rc = self._lib().hipEventCreateWithFlags(ctypes.byref(self._ev), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self):
+        import ctypes
+        import torch
+        rc = self._lib().hipEventRecord(self._ev, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end):
+        import ctypes
+        ms = ctypes.c_float()
+        rc = self._lib().hipEventElapsedTime(ctypes.byref(ms), self._ev, end._ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if getattr(self, "_ev", None) is not None and self._hip is not None:
+            self._hip.hipEventDestroy(self._ev)
+            self._ev = None
+
+
 def cpu_baseline(w, target_s=15.0):
     """Time the fp64 oracle on the first sequences of the workload (one thread)."""
     import oracle
@@ -219,6 +269,8 @@ def main():
                     help="replay each step's append and attention call as captured graphs")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the streaming-read ceiling probe run before the benchmark")
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="seconds of untimed steps before the warmup steps (steady clocks)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (to scale memory counters)")
     args = ap.parse_args()
@@ -345,12 +397,22 @@ def main():
             if i % args.layers == 0:
                 graph.launch()
 
+    # Bring the GPU to its steady clocks first: after the host-side workload generation the
+    # device has been idle for seconds, and a handful of steps is not enough for its clocks
+    # and power state to settle (the first steps then run up to ~20 % slower).  These steps
+    # are untimed, like the W warmup steps that follow.
+    settle_steps = 0
+    t_settle = time.time() + max(args.settle_s, 0.0)
+    while time.time() < t_settle:
+        for _ in range(args.layers):
+            step(settle_steps)
+            settle_steps += 1
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    evs = [(TimingEvent(), TimingEvent()) for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
@@ -433,7 +495,7 @@ def main():
             "kv_bytes_per_step": kvb, "flush_between_steps": bool(args.flush),
             "cache_copies_rotated": args.layers, "graph_replay": bool(args.graph),
             "quantizing_append": bool(append_fp8), "query_tokens_per_sequence": w.q_len,
-            "cascade": cascade,
+            "cascade": cascade, "settle_s": args.settle_s, "settle_steps": settle_steps,
         },
         "decode_tokens_per_s": round(w.B * w.q_len / (ms_per_step * 1e-3), 1),
         **({"decode_tokens_per_s_80_layers_kv_attention_only_excludes_weights":

@@ -31,6 +31,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void gqa_stream_kernel(DecodeArg
 // out[b][h] = sum over the pieces of segment (g = h / G, b) of 2^(m - M) o / 2^(m - M) l.
 // One wave per (sequence, query head), kMergeWaves of them per workgroup.
 constexpr int kMergeWaves = 4;
+constexpr int kFastPieces = 16;  // pieces per segment merged in a single round trip
 template <int D>
 __global__ __launch_bounds__(kMergeWaves * kWave) void stream_merge_kernel(DecodeArgs a) {
   constexpr int PER = D / kWave;
@@ -57,6 +58,56 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void stream_merge_kernel(Decod
     const long long cc = c0 + i;
     return T * cc / a.chunks != T * (cc + 1) / a.chunks;
   };
+  if constexpr (D <= 128) {
+    // Up to kFastPieces pieces: every piece's m, l and o row requested at once (one round
+    // trip), the weights formed afterwards; rows of pieces that carry no weight (empty
+    // chunks: never written) are loaded but not used.
+    constexpr int LPR = D / 4, RPW = kWave / LPR, U = kFastPieces / RPW;
+    if (np <= kFastPieces) {
+      const int sub = lane / LPR, col = lane % LPR;
+      float mp = kNegInf, lp = 0.f;
+      if (lane < np && live(lane)) {
+        mp = a.ws_m[(slot0 + lane) * G + h];
+        lp = a.ws_l[(slot0 + lane) * G + h];
+      }
+      float4 x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = u * RPW + sub;
+        x[u] = j < np ? *(const float4*)(a.ws_o + ((slot0 + j) * G + h) * D + 4 * col)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      float M = mp;
+#pragma unroll
+      for (int s = 32; s >= 1; s >>= 1) M = fmaxf(M, __shfl_xor(M, s));
+      const float f = (mp == kNegInf) ? 0.f : fast_exp2(mp - M);
+      float den = f * lp;
+#pragma unroll
+      for (int s = 32; s >= 1; s >>= 1) den += __shfl_xor(den, s);
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float fj = __shfl(f, u * RPW + sub);
+        if (fj != 0.f) {
+          acc.x += fj * x[u].x;
+          acc.y += fj * x[u].y;
+          acc.z += fj * x[u].z;
+          acc.w += fj * x[u].w;
+        }
+      }
+#pragma unroll
+      for (int m = LPR; m < kWave; m <<= 1) {
+        acc.x += __shfl_xor(acc.x, m);
+        acc.y += __shfl_xor(acc.y, m);
+        acc.z += __shfl_xor(acc.z, m);
+        acc.w += __shfl_xor(acc.w, m);
+      }
+      const float sc = den > 0.f ? 1.f / den : 0.f;
+      if (lane < LPR)
+        *(float4*)(out + 4 * lane) = make_float4(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
+      return;
+    }
+  }
   float M = kNegInf;
   for (int p0 = 0; p0 < np; p0 += kWave)
     if (p0 + lane < np && live(p0 + lane)) M = fmaxf(M, a.ws_m[(slot0 + p0 + lane) * G + h]);
