@@ -191,12 +191,22 @@ __device__ __forceinline__ void gqa_ring_body(const DecodeArgs& a, int bid, lds_
   uint32_t off_l[kRingTilesPerLane];
   int info_l[kRingTilesPerLane];  // valid tokens (5 bits) | segment << 5
   {
+    // head and tile-in-head of the lane's tiles: the chunk starts at head gg0, tile rem0 of
+    // it, and a lane's tile lies fewer than kRingMaxChunkTiles tiles further
+    const int Th = T_head > 0 ? T_head : 1;
+    const int gg0 = (int)(tb / Th), rem0 = (int)(tb - (long long)gg0 * Th);
     int lo_[kRingTilesPerLane], rem_[kRingTilesPerLane], gg_[kRingTilesPerLane];
 #pragma unroll
     for (int j = 0; j < kRingTilesPerLane; ++j) {
-      const long long t = tb + kWave * j + lane;
-      gg_[j] = (int)(t / (T_head > 0 ? T_head : 1));
-      rem_[j] = (int)(t - (long long)gg_[j] * T_head);
+      const uint32_t rr = (uint32_t)rem0 + kWave * j + lane;
+      if (Th >= kRingMaxChunkTiles) {  // at most one head boundary inside a chunk
+        const bool past = rr >= (uint32_t)Th;
+        gg_[j] = gg0 + past;
+        rem_[j] = (int)(past ? rr - Th : rr);
+      } else {
+        gg_[j] = gg0 + (int)(rr / (uint32_t)Th);
+        rem_[j] = (int)(rr % (uint32_t)Th);
+      }
       lo_[j] = 0;
     }
     // last sequence whose first tile is <= rem, for all of the lane's tiles at once
@@ -224,11 +234,13 @@ __device__ __forceinline__ void gqa_ring_body(const DecodeArgs& a, int bid, lds_
       if (n < ntl) {
         const int tt = rem_[j] - s_pre[lo_[j]];
         const int L = s_len[lo_[j]];
-        const int phys = a.block_table[(size_t)lo_[j] * a.max_blocks + tt / tiles_per_block];
+        const int blk = tiles_per_block == 1 ? tt : tt / tiles_per_block;
+        const int tin = tiles_per_block == 1 ? 0 : tt - blk * tiles_per_block;
+        const int phys = a.block_table[(size_t)lo_[j] * a.max_blocks + blk];
         const bool ok = (unsigned)phys < (unsigned)a.num_blocks;
         const uint64_t off = (uint64_t)(ok ? phys : 0) * block_bytes +
                              (uint64_t)gg_[j] * head_bytes +
-                             (uint64_t)(tt % tiles_per_block) * (kTile * Lo::ROW);
+                             (uint64_t)tin * (kTile * Lo::ROW);
         off_l[j] = (uint32_t)(off >> 8);
         info_l[j] = (ok ? min(kTile, L - tt * kTile) : 0) | ((gg_[j] * B + lo_[j]) << 5);
       }
