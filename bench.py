@@ -41,7 +41,8 @@ HBM_PEAK_GBS = 8000.0                       # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0              # MI355X dense bf16 / fp16 matrix peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
-    "gqa": ["paged_kv_cache_288_amd/csrc/gqa_stream.hip", "paged_kv_cache_288_amd/csrc/gqa_stream_body.hpp",
+    "gqa": ["paged_kv_cache_288_amd/csrc/gqa_stream.hip", "paged_kv_cache_288_amd/csrc/gqa_ring_body.hpp",
+            "paged_kv_cache_288_amd/csrc/gqa_stream_body.hpp",
             "paged_kv_cache_288_amd/csrc/gqa_decode.hip", "paged_kv_cache_288_amd/csrc/gqa_tile.hpp",
             "paged_kv_cache_288_amd/csrc/pkv_device.hpp"],
     "mla": ["paged_kv_cache_288_amd/csrc/mla_stream.hip", "paged_kv_cache_288_amd/csrc/gqa_stream.hip",
@@ -129,7 +130,7 @@ def kernel_label(w, pkv, ps, cascade=False):
             return "pkv_paged_decode_attn_mla call, balanced mode (mla_stream_kernel + stream_merge_kernel<512>)"
         return "pkv_paged_decode_attn_mla call, partitioned (mla_decode_kernel + partition_merge_kernel<512>)"
     if pkv.decode_partition_size(w.B, w.Hkv, w.max_context_len, ps) == 0:
-        return "pkv_paged_decode_attn call, balanced mode (gqa_stream_kernel + stream_merge_kernel)"
+        return "pkv_paged_decode_attn call, balanced mode (gqa_ring_kernel + stream_merge_kernel)"
     return "pkv_paged_decode_attn call, partitioned (gqa_decode_kernel + partition_merge_kernel)"
 
 
@@ -202,6 +203,25 @@ class TimingEvent:
             self._ev = None
 
 
+def cpu_model_name():
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    try:
+        r = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10)
+        for line in r.stdout.splitlines():
+            if line.strip().startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.TimeoutExpired):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, target_s=15.0):
     """Time the fp64 oracle on the first sequences of the workload (one thread)."""
     import oracle
@@ -241,6 +261,10 @@ def cpu_baseline(w, target_s=15.0):
         "value": round(tokens * per_token / t_total / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
+        "host_cpus": os.cpu_count(),
+        "cpu_model": cpu_model_name(),
+        "threads": ("one: BLAS and OpenMP pools limited to 1 thread with threadpoolctl"
+                    if limiter is not None else "one (threadpoolctl unavailable; numpy default)"),
         "kind": "oracle",
         "sample": f"first {done} of {w.B} sequences ({tokens} cached tokens, all {w.Hq} "
                   f"query heads x {w.q_len} query tokens), gather + fp64 attention, "
@@ -448,19 +472,29 @@ def main():
         "frac": round(achieved / HBM_PEAK_GBS, 4),
     }
     if w.kind == "mla":
-        # the latent case is a dense contraction on the matrix cores: scores (d_qk) and
-        # p.V (d_v) for every query head and cached token
+        # The latent case is a dense contraction on the matrix cores (scores over d_qk and
+        # p.V over d_v for every query head and cached token), but at about 240 flop per
+        # byte it sits below the ridge point of 8 TB/s and 2.5 PFLOP/s (312 flop/B): the
+        # binding roof is the larger of the two minimum times, and the fraction is that
+        # time over the call's.  Both rates are reported.
         flops = float(w.context_lens.astype(np.int64).sum()) * w.Hq * 2 * (w.d + w.d_v)
         tflops = flops / (call_avg * 1e-3) / 1e12
+        t_hbm = kvu / (HBM_PEAK_GBS * 1e9)
+        t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+        hbm_bound = t_hbm >= t_mfma
         roofline = {
-            "bound": "mfma",
-            "achieved": round(tflops, 2),
-            "peak": MFMA_BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "bound": "hbm" if hbm_bound else "mfma",
+            "achieved": round(achieved, 2) if hbm_bound else round(tflops, 2),
+            "peak": HBM_PEAK_GBS if hbm_bound else MFMA_BF16_PEAK_TFLOPS,
+            "unit": "GB/s" if hbm_bound else "TFLOP/s",
+            "frac": round(max(t_hbm, t_mfma) / (call_avg * 1e-3), 4),
+            "t_hbm_us": round(t_hbm * 1e6, 2),
+            "t_mfma_us": round(t_mfma * 1e6, 2),
             "algorithmic_flops_per_call": flops,
             "hbm_achieved_GBs": round(achieved, 2),
             "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
+            "mfma_achieved_TFLOPs": round(tflops, 2),
+            "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         }
     elif multi:
         # q_len * G query rows share each K/V row: scores and p.V on the matrix cores, still

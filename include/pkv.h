@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 
 typedef int32_t pkv_status;
 enum {
@@ -283,21 +283,32 @@ pkv_status pkv_paged_decode_attn_cascade(float* out, const void* q, const void* 
  * Cites: "深入LLM推理…" section "PagedAttention与Cache管理" (a sequence's table entries name
  * physical blocks of the pool; each new token gets its own slot).  The decode and append
  * calls never fault on bad values but their results are then unspecified; this call finds
- * them.  Writes four int32 counts to the device array counts[4]:
+ * them, and the values the decode calls would silently truncate or lose.  Writes six
+ * int32 counts to the device array counts[6]:
  *   counts[0]  table entries in use (the first ceil(L / block_size) of each row, L clamped to
  *              the table) outside [0, num_blocks)
  *   counts[1]  context lengths outside [0, max_blocks_per_seq * block_size]
  *   counts[2]  slots at or past num_blocks * block_size (negative slots mean "skip", legal)
  *   counts[3]  non-negative slots already used by an earlier token of the same append
  *              (quadratic in T: meant for checking, not for every step)
+ *   counts[4]  context lengths above max_context_len (the decode calls attend to the first
+ *              max_context_len tokens only); not checked when max_context_len < 0
+ *   counts[5]  bf16 values of V in use (the first d_v dims of each KV head's row of every
+ *              token within the clamped lengths, in blocks whose id is valid) of magnitude
+ *              65504 or more, infinities included: the p.V step widens V to fp16, where
+ *              they would become infinite; not checked when v_pool is NULL
  * block_table [B][max_blocks_per_seq], context_lens [B] int32; slot_mapping [T] int64 (may
- * be NULL when T = 0).  Enqueued on `stream` like the other calls; counts are valid once
- * the stream has passed the work.
+ * be NULL when T = 0); v_pool: a bf16 pool [num_blocks][Hkv][block_size][d] (the V pool,
+ * or a latent pool with Hkv = 1, d = 576, d_v = 512), or NULL; FP8 pools never overflow
+ * fp16 and need no check.  Enqueued on `stream` like the other calls; counts are valid once
+ * the stream has passed the work.  Errors: PKV_ERR_SHAPE, PKV_ERR_NULL, PKV_ERR_ALIGN,
+ * PKV_ERR_HIP.
  */
 pkv_status pkv_validate(int32_t* counts, const int32_t* block_table,
                         const int32_t* context_lens, int32_t B, int32_t max_blocks_per_seq,
-                        int32_t num_blocks, int32_t block_size, const int64_t* slot_mapping,
-                        int32_t T, void* stream);
+                        int32_t num_blocks, int32_t block_size, int32_t max_context_len,
+                        const int64_t* slot_mapping, int32_t T, const void* v_pool, int32_t Hkv,
+                        int32_t d, int32_t d_v, void* stream);
 
 /*
  * pkv_kv_append_fp8 — quantizing append ("PD 分离下的 KV Cache", "优化三：KV 传输优化": KV

@@ -60,8 +60,8 @@ _SIGNATURES = [
                                                  _c_int32, _c_int32, _c_int32, _c_int32,
                                                  _c_int32, _c_int32, _c_int32, _c_int32,
                                                  ctypes.c_float, _c_int32, _p, _c_size, _p]),
-    ("pkv_validate", _c_int32, [_p, _p, _p, _c_int32, _c_int32, _c_int32, _c_int32, _p, _c_int32,
-                                _p]),
+    ("pkv_validate", _c_int32, [_p, _p, _p, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _p,
+                                _c_int32, _p, _c_int32, _c_int32, _c_int32, _p]),
     ("pkv_kv_append_fp8", _c_int32, [_p, _p, _p, _p, _p, _p, _p, _c_int32, _c_int32, _c_int32,
                                      _c_int32, _c_int32, _p]),
     ("pkv_kv_copy_blocks", _c_int32, [_p, _p, _p, _p, _c_int32, _c_int32, _c_int32, _c_int32,
@@ -260,21 +260,33 @@ def paged_decode_attn_cascade(out, q, k_pool, v_pool, prefix_blocks, prefix_len,
     return out
 
 
-def validate(block_table, context_lens, num_blocks, block_size, slot_mapping=None):
+def validate(block_table, context_lens, num_blocks, block_size, slot_mapping=None,
+             max_context_len=-1, v_pool=None, d_v=None):
     """Count caller-contract violations on the device (pkv_validate): returns a dict with
     the table entries in use outside the pool, context lengths outside the table, slots
-    past the pool and slots written twice.  Synchronises the current stream."""
+    past the pool, slots written twice, context lengths above max_context_len (when it is
+    given, >= 0) and bf16 V values in use of magnitude 65504 or more (when v_pool, a bf16
+    pool [num_blocks, Hkv, block_size, d] or a latent pool [num_blocks, block_size, d], is
+    given; d_v leading dims checked, default all).  Synchronises the current stream."""
     import torch
-    counts = torch.empty(4, dtype=torch.int32, device=block_table.device)
+    counts = torch.empty(6, dtype=torch.int32, device=block_table.device)
     B, mb = block_table.shape
     T = 0 if slot_mapping is None else slot_mapping.shape[0]
+    Hkv = d = 0
+    if v_pool is not None:
+        if v_pool.dim() == 3:
+            Hkv, d = 1, v_pool.shape[2]
+        else:
+            Hkv, d = v_pool.shape[1], v_pool.shape[3]
+    dv = d if d_v is None else d_v
     st = load_library().pkv_validate(
         _ptr(counts), _ptr(block_table), _ptr(context_lens), B, mb, num_blocks, block_size,
-        _ptr(slot_mapping), T, _stream(block_table.device))
+        int(max_context_len), _ptr(slot_mapping), T, _ptr(v_pool), Hkv, d, dv,
+        _stream(block_table.device))
     _check("pkv_validate", st)
     c = counts.cpu().tolist()
     return {"bad_block_ids": c[0], "bad_context_lens": c[1], "slots_past_pool": c[2],
-            "duplicate_slots": c[3]}
+            "duplicate_slots": c[3], "lengths_above_max": c[4], "v_out_of_fp16_range": c[5]}
 
 
 def kv_append_fp8(k_pool, v_pool, k_new, v_new, k_scale, v_scale, slot_mapping):

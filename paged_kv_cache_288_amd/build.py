@@ -15,7 +15,6 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpkv.so")
 READ_CEILING = os.path.join(HERE, "read_ceiling")   # standalone bandwidth probe
-LDS_PROBE = os.path.join(HERE, "lds_probe")         # standalone LDS bank probe
 ARCH = "gfx950"
 
 SOURCES = ["pkv_api.hip", "kv_append.hip", "gqa_decode.hip", "gqa_stream.hip", "mla_decode.hip",
@@ -65,7 +64,7 @@ def build(isa=False, verbose=True):
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
-    for exe in (READ_CEILING, LDS_PROBE):
+    for exe in (READ_CEILING,):
         src = os.path.basename(exe) + ".hip"
         cmd = [HIPCC, *FLAGS, os.path.join(CSRC, src), "-o", exe + ".tmp"]
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -73,7 +72,7 @@ def build(isa=False, verbose=True):
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
         os.replace(exe + ".tmp", exe)
     if verbose:
-        print(f"built {LIB}, {READ_CEILING} and {LDS_PROBE}")
+        print(f"built {LIB} and {READ_CEILING}")
     return LIB
 
 

@@ -63,7 +63,8 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void gqa_decode_kernel(DecodeArg
   WaveState<D, G, FP8> S;
   load_q_reset<D, G, FP8>(S, a.q + ((size_t)b * a.Hq + (size_t)g * G) * D, c);
 
-  L = L < 0 ? 0 : (L > a.max_blocks * a.block_size ? a.max_blocks * a.block_size : L);
+  const int cap = min(a.max_blocks * a.block_size, a.max_context_len);
+  L = L < 0 ? 0 : (L > cap ? cap : L);
   if (t0 >= L) {
     if (a.num_partitions == 1 && part == 0) {  // empty sequence: output 0
       for (int idx = threadIdx.x; idx < G * D; idx += kWaves * kWave)

@@ -129,7 +129,7 @@ __device__ __forceinline__ void gqa_multi_body(const MultiArgs& a, int bid, int*
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int i16 = lane & 15, gq = lane >> 4;
   const int B = a.B, G = a.Hq / a.Hkv, R = G * a.q_len;
-  const int cap = a.max_blocks * a.block_size;
+  const int cap = min(a.max_blocks * a.block_size, a.max_len);
   auto seq_len = [&](int bi) {  // clamped to the table; one length for all in prefix mode
     int L = a.fixed_len >= 0 ? a.fixed_len : a.context_lens[bi];
     return L < 0 ? 0 : (L > cap ? cap : L);

@@ -23,7 +23,7 @@ __device__ __forceinline__ void gqa_stream_body(const DecodeArgs& a, int bid, in
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int k = lane >> 3, c = lane & 7, r = lane / Lo::LPT, dc = lane % Lo::LPT;
   const int B = a.B;
-  const int cap = a.max_blocks * a.block_size;
+  const int cap = min(a.max_blocks * a.block_size, a.max_context_len);
 
   // ---- tiles per sequence and their exclusive prefix, scanned across the workgroup
   auto ntiles = [&](int bi) {

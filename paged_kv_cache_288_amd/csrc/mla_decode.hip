@@ -105,7 +105,8 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void mla_decode_kernel(MlaArgs a
   const bool active = h0 < a.Hq;
 
   int L = a.context_lens[b];
-  L = L < 0 ? 0 : (L > a.max_blocks * a.block_size ? a.max_blocks * a.block_size : L);
+  const int cap = min(a.max_blocks * a.block_size, a.max_context_len);
+  L = L < 0 ? 0 : (L > cap ? cap : L);
   const int t0 = part * a.partition;
   if (t0 >= L) {
     if (a.num_partitions == 1 && part == 0 && active) {

@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_stream_kernel(MlaArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
   const int i16 = lane & 15, g = lane >> 4;
   const int B = a.B, Hq = a.Hq, HG = Hq / HPU, C = a.chunks;
-  const int cap = a.max_blocks * kBlock;
+  const int cap = min(a.max_blocks * kBlock, a.max_context_len);
 
   // ---- stages per sequence and their exclusive prefix (scratch in the stage buffers)
   int* s_pre = (int*)sbuf;
@@ -510,7 +510,7 @@ __global__ __launch_bounds__(8 * kWave, 1) void mla_split_kernel(MlaArgs a) {
   const int r4 = w & 3;  // head tile (scorer) or output-dim slice (accumulator)
   const int i16 = lane & 15, g = lane >> 4;
   const int B = a.B, Hq = a.Hq, HG = Hq / HPU, C = a.chunks;
-  const int cap = a.max_blocks * kBlock;
+  const int cap = min(a.max_blocks * kBlock, a.max_context_len);
 
   // ---- stages per sequence and their exclusive prefix.  Up to 64 sequences every wave
   // scans them in registers (lane i: sequence i), so that no workgroup barrier or LDS round

@@ -343,7 +343,7 @@ pkv_status pkv_paged_decode_attn(float* out, const void* q, const void* k_pool,
   if (st != PKV_OK || P == 1) return st;
   return hip_status(pkv::launch_partition_merge(ws_m, ws_l, ws_o, context_lens, out, B, Hq, d,
                                                 ps, P, ctx,
-                                                max_blocks_per_seq * block_size, s));
+                                                min(max_blocks_per_seq * block_size, ctx), s));
 }
 
 size_t pkv_mla_workspace_bytes(int32_t B, int32_t Hq, int32_t d_v, int32_t max_context_len,
@@ -414,7 +414,7 @@ pkv_status pkv_paged_decode_attn_mla(float* out, const void* q, const void* kv_p
   if (st != PKV_OK || P == 1) return st;
   return hip_status(pkv::launch_partition_merge(ws_m, ws_l, ws_o, context_lens, out, B, Hq, d_v,
                                                 ps, P, ctx,
-                                                max_blocks_per_seq * block_size, s));
+                                                min(max_blocks_per_seq * block_size, ctx), s));
 }
 
 size_t pkv_multi_workspace_bytes(int32_t B, int32_t q_len, int32_t Hq, int32_t Hkv, int32_t d,
@@ -471,6 +471,7 @@ pkv_status pkv_paged_decode_attn_multi(float* out, const void* q, const void* k_
   a.B = B, a.q_len = q_len, a.Hq = Hq, a.Hkv = Hkv, a.d = d, a.block_size = block_size;
   a.num_blocks = num_blocks, a.max_blocks = max_blocks_per_seq;
   a.table_stride = max_blocks_per_seq, a.fixed_len = -1, a.q_rows = B * q_len;
+  a.max_len = max_context_len;
   a.causal = 1, a.fp8 = fp8 ? 1 : 0, a.scale = scale, a.chunks = chunks;
   return hip_status(pkv::launch_gqa_multi(a, (hipStream_t)stream));
 }
@@ -548,6 +549,7 @@ pkv_status pkv_paged_decode_attn_cascade(float* out, const void* q, const void* 
     pa.B = c.p_B, pa.q_len = c.J, pa.Hq = Hq, pa.Hkv = Hkv, pa.d = d;
     pa.block_size = block_size, pa.num_blocks = num_blocks;
     pa.max_blocks = prefix_len / block_size, pa.table_stride = 0, pa.fixed_len = prefix_len;
+    pa.max_len = prefix_len;
     pa.q_rows = B, pa.causal = 0, pa.fp8 = fp8 ? 1 : 0, pa.scale = scale, pa.chunks = c.p_chunks;
     st = hip_status(pkv::launch_cascade(ta, pa, s));
   }
@@ -561,18 +563,21 @@ pkv_status pkv_paged_decode_attn_cascade(float* out, const void* q, const void* 
 
 pkv_status pkv_validate(int32_t* counts, const int32_t* block_table,
                         const int32_t* context_lens, int32_t B, int32_t max_blocks_per_seq,
-                        int32_t num_blocks, int32_t block_size, const int64_t* slot_mapping,
-                        int32_t T, void* stream) {
+                        int32_t num_blocks, int32_t block_size, int32_t max_context_len,
+                        const int64_t* slot_mapping, int32_t T, const void* v_pool, int32_t Hkv,
+                        int32_t d, int32_t d_v, void* stream) {
   if (B < 0 || T < 0 || num_blocks <= 0 || block_size <= 0 || max_blocks_per_seq < 0)
     return PKV_ERR_SHAPE;
+  if (v_pool && (Hkv <= 0 || d <= 0 || d_v <= 0 || d_v > d)) return PKV_ERR_SHAPE;
   if (!counts || (B > 0 && max_blocks_per_seq > 0 && (!block_table || !context_lens)) ||
       (T > 0 && !slot_mapping))
     return PKV_ERR_NULL;
   if (!aligned4(counts) || (B > 0 && (!aligned4(block_table) || !aligned4(context_lens))) ||
-      ((uintptr_t)slot_mapping & 7u))
+      ((uintptr_t)slot_mapping & 7u) || ((uintptr_t)v_pool & 1u))
     return PKV_ERR_ALIGN;
   pkv::ValidateArgs a{counts, block_table, context_lens, B, max_blocks_per_seq, num_blocks,
-                      block_size, slot_mapping, T};
+                      block_size, max_context_len, slot_mapping, T, (const uint16_t*)v_pool,
+                      Hkv, d, d_v};
   return hip_status(pkv::launch_validate(a, (hipStream_t)stream));
 }
 

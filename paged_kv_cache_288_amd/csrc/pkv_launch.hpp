@@ -102,12 +102,15 @@ hipError_t launch_mla_stream(const MlaArgs& a, hipStream_t s);
 
 // Debug check of block tables, context lengths and append slots (counts into counts[4]).
 struct ValidateArgs {
-  int32_t* counts;
+  int32_t* counts;  // [6]
   const int32_t* block_table;
   const int32_t* context_lens;
   int32_t B, max_blocks, num_blocks, block_size;
-  const int64_t* slots;  // may be null
+  int32_t max_context_len;  // < 0: not checked
+  const int64_t* slots;     // may be null
   int32_t T;
+  const uint16_t* v_pool;   // bf16 [num_blocks][Hkv][block_size][d], may be null
+  int32_t Hkv, d, d_v;      // first d_v dims of each row are the values checked
 };
 hipError_t launch_validate(const ValidateArgs& a, hipStream_t s);
 
@@ -133,6 +136,7 @@ struct MultiArgs {
   int32_t* ws_seg;     // [Hkv * B][2]
   int32_t B, q_len, Hq, Hkv, d, block_size, num_blocks;
   int32_t max_blocks;    // valid table entries per sequence
+  int32_t max_len;       // cap on context lengths (the host's max_context_len)
   int32_t table_stride;  // elements between table rows (0: one row shared by all)
   int32_t fixed_len;     // >= 0: every sequence has this length
   int32_t q_rows;        // real q rows along (b, j): B * q_len, fewer in prefix mode

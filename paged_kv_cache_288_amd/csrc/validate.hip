@@ -6,14 +6,19 @@
 // block of the pool and no two new tokens are written to the same slot.  The kernels never
 // fault on a bad value (out-of-range ids and slots are skipped, lengths clamped), but their
 // results are then unspecified; this call counts such values so that a caller can find
-// them.  Counting is by vector atomics into four device ints, zeroed by the first kernel.
+// them.  It also counts what the kernels would silently truncate or lose: context lengths
+// above the max_context_len a decode call is given (the kernels clamp to it) and bf16
+// values of V at or above fp16's largest finite magnitude (the p.V step widens V to fp16).
+// Counting is by vector atomics into six device ints, zeroed by the first kernel.
 #include "pkv_device.hpp"
 #include "pkv_launch.hpp"
 
 namespace pkv {
 
+constexpr int kCounts = 6;
+
 __global__ void validate_zero_kernel(int32_t* counts) {
-  if (threadIdx.x < 4) counts[threadIdx.x] = 0;
+  if (threadIdx.x < kCounts) counts[threadIdx.x] = 0;
 }
 
 // One thread per (sequence, table entry): counts[1] gets lengths outside
@@ -26,6 +31,7 @@ __global__ __launch_bounds__(256) void validate_tables_kernel(ValidateArgs a) {
   const int cap = a.max_blocks * a.block_size;
   int L = a.context_lens[b];
   if (j == 0 && (L < 0 || L > cap)) atomicAdd(&a.counts[1], 1);
+  if (j == 0 && a.max_context_len >= 0 && L > a.max_context_len) atomicAdd(&a.counts[4], 1);
   L = L < 0 ? 0 : (L > cap ? cap : L);
   if (j < (L + a.block_size - 1) / a.block_size) {
     const int phys = a.block_table[(size_t)b * a.max_blocks + j];
@@ -48,6 +54,33 @@ __global__ __launch_bounds__(256) void validate_slots_kernel(ValidateArgs a) {
     }
 }
 
+// One workgroup per (sequence, table entry in use): counts[5] gets the bf16 values among
+// the first d_v dims of every KV head's rows of that block's tokens in use (L clamped to
+// the table and to max_context_len) whose magnitude is 65504 or more, infinities included
+// (bf16 has no value between 65280 and 65536, so that is |bits| in [0x4780, 0x7F80]).
+__global__ __launch_bounds__(256) void validate_values_kernel(ValidateArgs a) {
+  const int b = blockIdx.x / a.max_blocks, j = blockIdx.x % a.max_blocks;
+  const int cap = a.max_blocks * a.block_size;
+  int L = a.context_lens[b];
+  L = L < 0 ? 0 : (L > cap ? cap : L);
+  if (a.max_context_len >= 0 && L > a.max_context_len) L = a.max_context_len;
+  const int t0 = j * a.block_size;
+  if (t0 >= L) return;
+  const int phys = a.block_table[(size_t)b * a.max_blocks + j];
+  if (phys < 0 || phys >= a.num_blocks) return;
+  const int ntok = min(a.block_size, L - t0);
+  const long long n = (long long)a.Hkv * ntok * a.d_v;
+  int found = 0;
+  for (long long e = threadIdx.x; e < n; e += blockDim.x) {
+    const int i = (int)(e % a.d_v);
+    const long long r = e / a.d_v;
+    const int t = (int)(r % ntok), h = (int)(r / ntok);
+    const uint16_t x = a.v_pool[(((size_t)phys * a.Hkv + h) * a.block_size + t) * a.d + i] & 0x7FFF;
+    found += (x >= 0x4780 && x <= 0x7F80);
+  }
+  if (found) atomicAdd(&a.counts[5], found);
+}
+
 hipError_t launch_validate(const ValidateArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(validate_zero_kernel, dim3(1), dim3(64), 0, s, a.counts);
   hipError_t e = hipGetLastError();
@@ -61,6 +94,11 @@ hipError_t launch_validate(const ValidateArgs& a, hipStream_t s) {
   }
   if (a.T > 0 && a.slots) {
     hipLaunchKernelGGL(validate_slots_kernel, dim3((unsigned)((a.T + 255) / 256)), dim3(256), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.v_pool && entries > 0) {
+    hipLaunchKernelGGL(validate_values_kernel, dim3((unsigned)entries), dim3(256), 0, s, a);
     e = hipGetLastError();
   }
   return e;

@@ -112,3 +112,7 @@ def assert_close(got, ref, kv_dtype, what=""):
     log(f"  {what}: max|err|={err.max():.3e} normwise={normwise:.3e} "
         f"worst at {worst}: got {got[worst]:.6g} ref {ref[worst]:.6g}")
     assert (err <= bound).all(), f"{what}: {int((err > bound).sum())} elements out of tolerance"
+    if kv_dtype == "fp8":
+        # the FP8 bound is relative; the absolute floor above is a large share of the small
+        # outputs of long contexts, so the bound is also checked normwise
+        assert err.max() <= rel * np.abs(ref).max(), f"{what}: normwise error {normwise:.3e} > {rel}"

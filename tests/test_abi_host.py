@@ -114,10 +114,11 @@ def test_partition_and_workspace_sizing(lib):
     assert lib.pkv_decode_partition_size(1, 8, 100, 20) < 0
 
 
-def _stream_chunks(B, Hkv, ctx, cus):
-    """One chunk per wave (8 per CU), at most the bound on the tiles, at most 128 tiles each."""
+def _stream_chunks(B, Hkv, ctx, cus, waves_per_cu=4, max_tiles=256):
+    """One chunk per wave (the decode kernel runs one wave per SIMD: 4 per CU), at most the
+    bound on the tiles, at most 256 tiles each, a multiple of 32."""
     tmax = Hkv * B * ((ctx + 15) // 16)
-    c = max(min(8 * cus, tmax), -(-tmax // 128))
+    c = max(min(waves_per_cu * cus, tmax), -(-tmax // max_tiles))
     return max(32, -(-c // 32) * 32)
 
 
@@ -352,8 +353,8 @@ def test_cascade_workspace_size(lib):
 
 def test_validate_rejects_bad_arguments_before_launch(lib):
     f = lib.pkv_validate
-    # counts table lens B mb nb bs slots T stream
-    base = [FAKE, FAKE, FAKE, 4, 8, 100, 16, FAKE, 10, None]
+    # counts table lens B mb nb bs max_ctx slots T v_pool Hkv d d_v stream
+    base = [FAKE, FAKE, FAKE, 4, 8, 100, 16, 128, FAKE, 10, None, 0, 0, 0, None]
     def call(**kw):
         a = list(base)
         for i, v in kw.items():
@@ -364,6 +365,9 @@ def test_validate_rejects_bad_arguments_before_launch(lib):
     assert call(a6=0) == -2
     assert call(a0=None) == -1
     assert call(a1=None) == -1
-    assert call(a7=None) == -1           # T > 0 needs slots
+    assert call(a8=None) == -1           # T > 0 needs slots
     assert call(a0=ctypes.c_void_p(0x1002)) == -5   # counts must be 4-byte aligned
-    assert call(a7=ctypes.c_void_p(0x1004)) == -5   # slots must be 8-byte aligned
+    assert call(a8=ctypes.c_void_p(0x1004)) == -5   # slots must be 8-byte aligned
+    assert call(a10=FAKE, a11=0, a12=128, a13=128) == -2   # a V pool needs its shape
+    assert call(a10=FAKE, a11=8, a12=128, a13=129) == -2   # d_v <= d
+    assert call(a10=ctypes.c_void_p(0x1001), a11=8, a12=128, a13=128) == -5

@@ -10,22 +10,28 @@ from gpu_common import log, make_workload, torch_cuda
 pytestmark = pytest.mark.gpu
 
 
-def _run(torch, table, lens, num_blocks, bs, slots=None):
+def _run(torch, table, lens, num_blocks, bs, slots=None, max_context_len=-1, v_pool=None, d_v=None):
     import paged_kv_cache_288_amd as pkv
     t = torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32)).cuda()
     l = torch.from_numpy(np.ascontiguousarray(lens, dtype=np.int32)).cuda()
     s = None if slots is None else torch.from_numpy(np.ascontiguousarray(slots, dtype=np.int64)).cuda()
-    return pkv.validate(t, l, num_blocks, bs, s)
+    v = None if v_pool is None else torch.from_numpy(np.ascontiguousarray(v_pool).view(np.int16)).cuda()
+    return pkv.validate(t, l, num_blocks, bs, s, max_context_len, v, d_v)
+
+
+CLEAN = {"bad_block_ids": 0, "bad_context_lens": 0, "slots_past_pool": 0, "duplicate_slots": 0,
+         "lengths_above_max": 0, "v_out_of_fp16_range": 0}
 
 
 def test_clean_workload_counts_nothing():
     torch = torch_cuda()
     for name in ("gqa70b", "fp8prefix", "tiny"):
         w = make_workload(name, seed=1, B=8) if name != "tiny" else make_workload(name)
-        got = _run(torch, w.block_table, w.context_lens, w.num_blocks, w.bs, w.slot_mapping)
+        vp = w.v_pool if w.kv_dtype == "bf16" else None
+        got = _run(torch, w.block_table, w.context_lens, w.num_blocks, w.bs, w.slot_mapping,
+                   w.max_context_len, vp)
         log(f"[validate] {name}: {got}")
-        assert got == {"bad_block_ids": 0, "bad_context_lens": 0, "slots_past_pool": 0,
-                       "duplicate_slots": 0}
+        assert got == CLEAN
 
 
 def test_planted_violations_are_counted():
@@ -42,7 +48,39 @@ def test_planted_violations_are_counted():
     got = _run(torch, table, lens, nb, bs, slots)
     log(f"[validate] planted: {got}")
     assert got == {"bad_block_ids": 3, "bad_context_lens": 1, "slots_past_pool": 1,
-                   "duplicate_slots": 3}
+                   "duplicate_slots": 3, "lengths_above_max": 0, "v_out_of_fp16_range": 0}
     lens2 = lens.copy()
     lens2[2] = -4
     assert _run(torch, table, lens2, nb, bs)["bad_context_lens"] == 2
+
+
+def test_lengths_above_max_and_v_out_of_fp16_range_are_counted():
+    """Planted: two context lengths above max_context_len; bf16 V values of 65536, -65536
+    and +-inf inside the lengths in use (counted), 65280 (the largest bf16 below 65504: not
+    counted), NaN (not counted), and 65536 past a sequence's length or past
+    max_context_len (not counted)."""
+    torch = torch_cuda()
+    w = make_workload("gqa70b", seed=3, B=4, lens=("fixed", [40, 70, 33, 16]), heads=(16, 2))
+    v = w.v_pool.view(np.uint16).copy()
+    v[v == 0x7FC0] = 0          # the poison outside the histories is NaN: clear it
+    def put(b, t, h, i, bits):
+        v[w.block_table[b, t // w.bs], h, t % w.bs, i] = bits
+    put(0, 3, 0, 5, 0x4780)     # 65536: counted
+    put(1, 69, 1, 127, 0xC780)  # -65536: counted
+    put(2, 0, 0, 0, 0x7F80)     # +inf: counted
+    put(2, 32, 1, 64, 0xFF80)   # -inf: counted
+    put(0, 10, 1, 7, 0x477F)    # 65280: fits fp16, not counted
+    put(1, 5, 0, 9, 0x7FC1)     # NaN: not counted
+    put(0, 41, 0, 0, 0x4780)    # past sequence 0's 40 tokens: not in use
+    lens = np.array([40, 70, 33, 16], dtype=np.int32)
+    got = _run(torch, w.block_table, lens, w.num_blocks, w.bs, None, 64, v)
+    log(f"[validate] planted values: {got}")
+    # lengths above 64: sequence 1 (70); its token 69 lies past 64, so that value is not counted
+    assert got["lengths_above_max"] == 1
+    assert got["v_out_of_fp16_range"] == 3
+    got = _run(torch, w.block_table, lens, w.num_blocks, w.bs, None, 80, v)
+    assert got["lengths_above_max"] == 0 and got["v_out_of_fp16_range"] == 4
+    # only the first d_v dims of each row are values: d_v = 64 leaves out dims 64.. of the rows
+    got = _run(torch, w.block_table, lens, w.num_blocks, w.bs, None, 80, v, d_v=64)
+    assert got["v_out_of_fp16_range"] == 2
+    assert _run(torch, w.block_table, lens, w.num_blocks, w.bs)["v_out_of_fp16_range"] == 0
