@@ -157,6 +157,33 @@ pkv_status pkv_paged_decode_attn(float* out, const void* q, const void* k_pool,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pkv_paged_decode_attn_noalloc — pkv_paged_decode_attn for callers that cannot allocate
+ * device memory: code running under HIP graph capture, serving loops that must not call
+ * hipMalloc, harnesses that forbid it.  Same arguments, meaning, layouts, precision and
+ * errors as pkv_paged_decode_attn, without the workspace: the call uses a device-resident
+ * scratch array of the library, PKV_NOALLOC_SCRATCH_BYTES bytes per GPU, held from the
+ * first call on that GPU until the process ends.  Nothing is allocated by the call.
+ *
+ * Returns PKV_ERR_WORKSPACE when pkv_decode_workspace_bytes for these arguments exceeds
+ * PKV_NOALLOC_SCRATCH_BYTES (e.g. the balanced mode of 64 sequences x 8 KV heads x 64
+ * query heads needs 6.4 MB), and PKV_ERR_HIP when the scratch's device address cannot be
+ * obtained.  Every call on one GPU shares that GPU's scratch, which keeps the last call's
+ * contents (the kernels need it in no particular state): calls that overlap in time on
+ * one GPU (on different streams, or from different threads) race and give unspecified
+ * results.  The call keeps one device address per GPU; it is safe to call from several
+ * host threads as long as their GPU work does not overlap.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (16 << 20)
+pkv_status pkv_paged_decode_attn_noalloc(float* out, const void* q, const void* k_pool,
+                                         const void* v_pool, const float* k_scale,
+                                         const float* v_scale, const int32_t* block_table,
+                                         const int32_t* context_lens, int32_t B, int32_t Hq,
+                                         int32_t Hkv, int32_t d, int32_t block_size,
+                                         int32_t num_blocks, int32_t max_blocks_per_seq,
+                                         int32_t max_context_len, float scale, int32_t kv_dtype,
+                                         int32_t partition_size, void* stream);
+
+/*
  * pkv_mla_workspace_bytes — workspace bytes for pkv_paged_decode_attn_mla with these
  * arguments (0 when the context is not split).
  */

@@ -13,7 +13,7 @@ import os
 __all__ = [
     "PKV_BF16", "PKV_FP8_E4M3", "PkvError", "library_path", "load_library",
     "abi_version", "kv_append", "decode_partition_size", "decode_workspace_bytes",
-    "paged_decode_attn", "mla_workspace_bytes", "paged_decode_attn_mla", "Graph",
+    "paged_decode_attn", "paged_decode_attn_noalloc", "mla_workspace_bytes", "paged_decode_attn_mla", "Graph",
     "graph_begin", "graph_end", "graph_launch", "graph_destroy", "kv_append_fp8",
     "kv_copy_blocks", "block_hashes", "multi_workspace_bytes", "paged_decode_attn_multi",
     "cascade_workspace_bytes", "paged_decode_attn_cascade", "validate",
@@ -44,6 +44,10 @@ _SIGNATURES = [
                                          _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
                                          _c_int32, ctypes.c_float, _c_int32, _c_int32, _p,
                                          _c_size, _p]),
+    ("pkv_paged_decode_attn_noalloc", _c_int32, [_p, _p, _p, _p, _p, _p, _p, _p, _c_int32,
+                                                 _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+                                                 _c_int32, _c_int32, ctypes.c_float, _c_int32,
+                                                 _c_int32, _p]),
     ("pkv_mla_workspace_bytes", _c_size, [_c_int32, _c_int32, _c_int32, _c_int32, _c_int32]),
     ("pkv_paged_decode_attn_mla", _c_int32, [_p, _p, _p, _p, _p, _c_int32, _c_int32, _c_int32,
                                              _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
@@ -183,6 +187,23 @@ def paged_decode_attn(out, q, k_pool, v_pool, block_table, context_lens, scale, 
         block_table.shape[1], max_context_len, float(scale), _dtype_code(kv_dtype),
         partition_size, _ptr(workspace), wsize, _stream(q.device))
     _check("pkv_paged_decode_attn", st)
+    return out
+
+
+def paged_decode_attn_noalloc(out, q, k_pool, v_pool, block_table, context_lens, scale,
+                              max_context_len, kv_dtype="bf16", k_scale=None, v_scale=None,
+                              partition_size=0):
+    """out[B, Hq, d] (fp32) = paged decode attention through pkv_paged_decode_attn_noalloc:
+    the same computation as paged_decode_attn, with the library's device scratch
+    (PKV_NOALLOC_SCRATCH_BYTES per GPU) as the workspace; nothing is allocated."""
+    B, Hq, d = q.shape
+    num_blocks, Hkv, bs, _ = k_pool.shape
+    st = load_library().pkv_paged_decode_attn_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_table), _ptr(context_lens), B, Hq, Hkv, d, bs, num_blocks,
+        block_table.shape[1], max_context_len, float(scale), _dtype_code(kv_dtype),
+        partition_size, _stream(q.device))
+    _check("pkv_paged_decode_attn_noalloc", st)
     return out
 
 

@@ -4,12 +4,37 @@
 // of decode steps as HIP graphs.
 #include <stdint.h>
 
+#include <mutex>
 #include <new>
 
 #include "../../include/pkv.h"
 #include "pkv_launch.hpp"
 
+// Device-resident scratch for pkv_paged_decode_attn_noalloc: every GPU the library runs on
+// holds one copy until the process ends.  Host code never passes `scratch` itself to a
+// kernel (in host code the name stands for a host-side shadow, not a device address): the
+// per-device address comes from hipGetSymbolAddress, taken once per device with that
+// device current.
+static __device__ __align__(256) uint8_t scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (nullptr on failure).
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
 
 constexpr int kMaxPartitionTokens = 4096;  // 64 tiles of 16 tokens per wave, 4 waves
 constexpr int kMaxStreamSeqs = 4096;       // balanced mode: sequences per call
@@ -344,6 +369,32 @@ pkv_status pkv_paged_decode_attn(float* out, const void* q, const void* k_pool,
   return hip_status(pkv::launch_partition_merge(ws_m, ws_l, ws_o, context_lens, out, B, Hq, d,
                                                 ps, P, ctx,
                                                 min(max_blocks_per_seq * block_size, ctx), s));
+}
+
+pkv_status pkv_paged_decode_attn_noalloc(float* out, const void* q, const void* k_pool,
+                                         const void* v_pool, const float* k_scale,
+                                         const float* v_scale, const int32_t* block_table,
+                                         const int32_t* context_lens, int32_t B, int32_t Hq,
+                                         int32_t Hkv, int32_t d, int32_t block_size,
+                                         int32_t num_blocks, int32_t max_blocks_per_seq,
+                                         int32_t max_context_len, float scale, int32_t kv_dtype,
+                                         int32_t partition_size, void* stream) {
+  // the same argument checks and the same kernels as pkv_paged_decode_attn, with the
+  // library's device scratch as the workspace (no allocation anywhere on this path)
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_context_len < 0 || Hq % Hkv)
+    return PKV_ERR_SHAPE;
+  const size_t need = pkv_decode_workspace_bytes(B, Hq, Hkv, d, max_context_len, partition_size);
+  if (need > (size_t)PKV_NOALLOC_SCRATCH_BYTES) return PKV_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0 && B > 0) {
+    ws = scratch_on_current_device();
+    if (!ws) return PKV_ERR_HIP;
+  }
+  return pkv_paged_decode_attn(out, q, k_pool, v_pool, k_scale, v_scale, block_table,
+                               context_lens, B, Hq, Hkv, d, block_size, num_blocks,
+                               max_blocks_per_seq, max_context_len, scale, kv_dtype,
+                               partition_size, ws, ws ? (size_t)PKV_NOALLOC_SCRATCH_BYTES : 0,
+                               stream);
 }
 
 size_t pkv_mla_workspace_bytes(int32_t B, int32_t Hq, int32_t d_v, int32_t max_context_len,

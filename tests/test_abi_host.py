@@ -371,3 +371,17 @@ def test_validate_rejects_bad_arguments_before_launch(lib):
     assert call(a10=FAKE, a11=0, a12=128, a13=128) == -2   # a V pool needs its shape
     assert call(a10=FAKE, a11=8, a12=128, a13=129) == -2   # d_v <= d
     assert call(a10=ctypes.c_void_p(0x1001), a11=8, a12=128, a13=128) == -5
+
+def test_noalloc_rejects_what_exceeds_its_scratch(lib):
+    """The allocation-free decode call refuses, before any GPU work, an argument set whose
+    workspace would exceed the library's scratch (4096 sequences of 32K tokens, 8 KV heads)."""
+    scratch = int(re.search(r"#define PKV_NOALLOC_SCRATCH_BYTES \((\d+) << (\d+)\)",
+                            open(HEADER).read()).expand(r"\1")) << 20
+    assert lib.pkv_decode_workspace_bytes(4096, 64, 8, 128, 32768, 0) > scratch
+    st = lib.pkv_paged_decode_attn_noalloc(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 4096,
+                                           64, 8, 128, 16, 10, 2048, 32768, 0.1, pkv.PKV_BF16,
+                                           0, None)
+    assert st == pkv.PKV_ERR_WORKSPACE
+    assert lib.pkv_paged_decode_attn_noalloc(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 4,
+                                             64, 12, 128, 16, 10, 64, 1024, 0.1, pkv.PKV_BF16,
+                                             0, None) == pkv.PKV_ERR_SHAPE
