@@ -23,8 +23,8 @@ namespace pkv {
 
 constexpr int kRing = 3;           // tiles in flight per wave (default)
 constexpr int kRingWaves = 4;      // waves per workgroup, one workgroup per CU (default)
-constexpr int kRingTilesPerLane = 4;
-constexpr int kRingMaxChunkTiles = kWave * kRingTilesPerLane;  // 256
+constexpr int kRingTilesPerLane = 8;
+constexpr int kRingMaxChunkTiles = kWave * kRingTilesPerLane;  // 512
 constexpr int kRingMaxSeqs = 4096;
 
 typedef __attribute__((ext_vector_type(4))) int i32x4_t;
@@ -126,7 +126,6 @@ __device__ __forceinline__ void gqa_ring_body(const DecodeArgs& a, int bid, lds_
   using R = Ring<D, G, FP8, NS>;
   static_assert(NS >= 2 && NS <= 4, "ring depth");
   static_assert(WPG == 4 || WPG == 8, "waves per workgroup");
-  static_assert(kRingTilesPerLane == 4, "per-lane tile tables are selected four ways");
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int k = lane >> 3, c = lane & 7, r = lane / Lo::LPT, dc = lane % Lo::LPT;
@@ -328,29 +327,27 @@ __device__ __forceinline__ void gqa_ring_body(const DecodeArgs& a, int bid, lds_
     S.l = 0.f;
   };
 
-  // ---- per-tile tables of the 64-tile block holding the current tile and of the next one
-  // (the per-lane arrays are selected once per block; every lookup below is a readlane)
-  int cur_info = 0, nxt_info = 0;
-  uint32_t cur_off = 0, nxt_off = 0;
-  uint64_t cur_st = 0, nxt_st = 0;
-  auto select_block = [&](int j) {
-    auto pick = [&](auto const (&x)[kRingTilesPerLane], int i) {
-      return i == 0 ? x[0] : (i == 1 ? x[1] : (i == 2 ? x[2] : (i == 3 ? x[3] : 0)));
-    };
-    cur_info = pick(info_l, j);
-    nxt_info = pick(info_l, j + 1);
-    cur_off = pick(off_l, j);
-    nxt_off = pick(off_l, j + 1);
-    cur_st = j == 0 ? starts[0] : (j == 1 ? starts[1] : (j == 2 ? starts[2] : starts[3]));
-    nxt_st = j == 0 ? starts[1] : (j == 1 ? starts[2] : (j == 2 ? starts[3] : 0));
+  // ---- per-tile tables of the 64-tile block holding the current tile (entry 0 of the
+  // per-lane arrays) and of the next one (entry 1): at each block boundary the arrays move
+  // down by one entry, so every lookup below is a readlane of a fixed register
+  auto next_block = [&]() {
+#pragma unroll
+    for (int q = 0; q + 1 < kRingTilesPerLane; ++q) {
+      info_l[q] = info_l[q + 1];
+      off_l[q] = off_l[q + 1];
+      starts[q] = starts[q + 1];
+    }
+    info_l[kRingTilesPerLane - 1] = 0;
+    off_l[kRingTilesPerLane - 1] = 0;
+    starts[kRingTilesPerLane - 1] = 0;
   };
   // Requests tile ln + NS of the current block (past the chunk's end: zeros) into ring slot
   // s, preceded by the q rows of its piece when it opens one (into q slot qs).
   auto issue = [&](int ln, int s, bool opens, int& qs) {
     const int p = ln + NS, pl = p & (kWave - 1);
     const bool nb = p >= kWave;
-    const int info = __builtin_amdgcn_readlane(nb ? nxt_info : cur_info, pl);
-    const uint64_t off = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(nb ? nxt_off : cur_off), pl) << 8;
+    const int info = __builtin_amdgcn_readlane(nb ? info_l[1] : info_l[0], pl);
+    const uint64_t off = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(nb ? off_l[1] : off_l[0]), pl) << 8;
     if (opens) {
       const int sg = info >> 5, gg = sg / B, bb = sg - gg * B;
       const uint16_t* qg = a.q + ((size_t)bb * a.Hq + (size_t)gg * G) * D;
@@ -374,15 +371,14 @@ __device__ __forceinline__ void gqa_ring_body(const DecodeArgs& a, int bid, lds_
   // ---- the walk.  The first NS tiles are requested up front; then per tile: wait for its
   // slot, read it (and at a piece start the piece's q), request tile n + NS into the slot,
   // compute, and at a piece end write the piece.
-  select_block(0);
   int q_issue = 0, q_read = 0;
   {
     // tiles 0 .. NS-1, as issue() would for ln = -NS .. -1
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
-      const int info = __builtin_amdgcn_readlane(cur_info, t);
-      const uint64_t off = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)cur_off, t) << 8;
-      if ((cur_st >> t) & 1) {
+      const int info = __builtin_amdgcn_readlane(info_l[0], t);
+      const uint64_t off = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)off_l[0], t) << 8;
+      if ((starts[0] >> t) & 1) {
         const int sg = info >> 5, gg = sg / B, bb = sg - gg * B;
         const uint16_t* qg = a.q + ((size_t)bb * a.Hq + (size_t)gg * G) * D;
         const i32x4_t qr = ring_rsrc(qg, R::QB);
@@ -408,15 +404,15 @@ __device__ __forceinline__ void gqa_ring_body(const DecodeArgs& a, int bid, lds_
   int s = 0;
   for (int n = 0; n < ntl; ++n) {
     const int ln = n & (kWave - 1);
-    if (ln == 0 && n) select_block(n >> 6);
+    if (ln == 0 && n) next_block();
     // start bits of tiles n, n+1, ... (the next 64)
-    const uint64_t win = (cur_st >> ln) | (ln ? nxt_st << (kWave - ln) : 0ull);
+    const uint64_t win = (starts[0] >> ln) | (ln ? starts[1] << (kWave - ln) : 0ull);
     // outstanding after tile n's copies: tiles n+1 .. n+NS-1 and the q copies among them
     wait_vm_dyn<(NS - 1) * R::LOADS, R::QCOPIES, NS - 1>(__builtin_popcountll(win & kAheadMask));
     compiler_fence();
     TileRegs<D, FP8> RT;
     read_tile(RT, s);
-    const int info = __builtin_amdgcn_readlane(cur_info, ln);
+    const int info = __builtin_amdgcn_readlane(info_l[0], ln);
     if (win & 1) {
       seg = info >> 5;
       read_q(S, q_read);

@@ -135,19 +135,38 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void stream_merge_kernel(Decod
   rows_store<D>(acc, out, den > 0.f ? 1.f / den : 0.f, lane);
 }
 
-// The library's default single-token decode: one workgroup of kRingWaves waves per CU,
-// each wave streaming its chunk through an LDS ring (gqa_ring_body.hpp).
+// The library's default single-token decode: one workgroup per CU, each wave streaming its
+// chunk through an LDS ring (gqa_ring_body.hpp).  With 8 query heads per KV head a tile's
+// arithmetic keeps one wave busy while three tiles are in flight: 4 waves (one per SIMD)
+// with 3-tile rings, up to 512 registers each.  Smaller groups have lighter tiles, whose
+// arithmetic a single wave cannot hide when their data comes from L2 (a shared prefix
+// re-read): there two waves per SIMD, 2-tile rings, hide each other's arithmetic.
 template <int D, int G, bool FP8>
-__global__ __launch_bounds__(kRingWaves * kWave, 1) void gqa_ring_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t s_lds[ring_lds_bytes<D, G, FP8>()];
-  gqa_ring_body<D, G, FP8>(a, blockIdx.x, (lds_u8_t*)s_lds);
+struct RingShape {
+  static constexpr int WPG = G == 8 ? 4 : 8;
+  static constexpr int NS = WPG == 4 ? 3 : 2;
+};
+int ring_waves_per_cu(int d, int G, bool fp8) {
+  (void)d;
+  (void)fp8;
+  return G == 8 ? 4 : 8;
+}
+
+template <int D, int G, bool FP8>
+__global__ __launch_bounds__((RingShape<D, G, FP8>::WPG * kWave), 1) void gqa_ring_kernel(DecodeArgs a) {
+  using RS = RingShape<D, G, FP8>;
+  __shared__ __attribute__((aligned(1024))) uint8_t s_lds[ring_lds_bytes<D, G, FP8, RS::NS, RS::WPG>()];
+  gqa_ring_body<D, G, FP8, RS::NS, RS::WPG>(a, blockIdx.x, (lds_u8_t*)s_lds);
 }
 
 template <int D, int G, bool FP8>
 static hipError_t launch_stream_one(const DecodeArgs& a, hipStream_t s, bool merge) {
   if (merge) {
-    hipLaunchKernelGGL((gqa_ring_kernel<D, G, FP8>), dim3(a.chunks / kRingWaves),
-                       dim3(kRingWaves * kWave), 0, s, a);
+    constexpr int WPG = RingShape<D, G, FP8>::WPG;
+    // chunk = (XCD eighth) + (workgroup within it) * WPG + wave: whole workgroups per eighth
+    if (a.chunks % (8 * WPG) || a.B > kRingMaxSeqs) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gqa_ring_kernel<D, G, FP8>), dim3(a.chunks / WPG), dim3(WPG * kWave), 0,
+                       s, a);
   } else {
     hipLaunchKernelGGL((gqa_stream_kernel<D, G, FP8>), dim3(a.chunks / kWaves),
                        dim3(kWaves * kWave), 0, s, a);

@@ -39,10 +39,10 @@ void* scratch_on_current_device() {
 constexpr int kMaxPartitionTokens = 4096;  // 64 tiles of 16 tokens per wave, 4 waves
 constexpr int kMaxStreamSeqs = 4096;       // balanced mode: sequences per call
 constexpr long long kMaxChunkTiles = 128;  // balanced mode: tiles per wave
-constexpr int kRingWavesPerCu = 4;         // the default decode kernel: one wave per SIMD
-constexpr long long kRingChunkTiles = 256; // and up to 256 tiles per wave
+constexpr int kRingMaxWavesPerCu = 8;      // the default decode kernel: 4 or 8 waves per CU
+constexpr long long kRingChunkTiles = 512; // and up to 512 tiles per wave
 
-int32_t ring_chunks(int32_t B, int32_t Hkv, int32_t max_ctx);
+int32_t ring_chunks(int32_t B, int32_t Hkv, int32_t max_ctx, int waves_per_cu);
 constexpr int kGridYZMax = 65535;
 constexpr long long kTargetWorkgroups = 1024;  // ~4 workgroups per CU on 256 CUs
 
@@ -116,22 +116,26 @@ int device_cus() {
 // Balanced mode: one chunk per resident wave (two 4-wave workgroups per CU for the
 // single-token kernel), and enough chunks that
 // none holds more than kMaxChunkTiles tiles even if every context were max_context_len;
-// never more chunks than that bound on the tiles (rounded up to 32), so that a small
-// batch is not spread over thousands of empty chunks the merge would walk.
+// never more chunks than that bound on the tiles (rounded up to 8 workgroups), so that a
+// small batch is not spread over thousands of empty chunks the merge would walk.
 int32_t stream_chunks(int32_t B, int32_t Hkv, int32_t max_ctx, int waves_per_cu = 8,
-                      long long max_chunk_tiles = kMaxChunkTiles) {
+                      long long max_chunk_tiles = kMaxChunkTiles, int waves_per_group = 4) {
   const long long tmax = (long long)Hkv * B * ((max_ctx + 15) / 16);
   long long c = (long long)waves_per_cu * device_cus();
   if (tmax < c) c = tmax;
   const long long need = (tmax + max_chunk_tiles - 1) / max_chunk_tiles;
   if (need > c) c = need;
-  c = (c + 31) / 32 * 32;
-  if (c < 32) c = 32;
+  // a multiple of 8 workgroups' worth: each of the 8 XCDs takes whole workgroups of an eighth
+  const long long unit = 8LL * waves_per_group;
+  c = (c + unit - 1) / unit * unit;
+  if (c < unit) c = unit;
   return c > (1LL << 30) ? -1 : (int32_t)c;
 }
 
-int32_t ring_chunks(int32_t B, int32_t Hkv, int32_t max_ctx) {
-  return stream_chunks(B, Hkv, max_ctx, kRingWavesPerCu, kRingChunkTiles);
+// The decode kernel's chunks; the workspace query sizes for the largest count (8 waves per
+// CU), since it does not know the element type that selects the kernel's shape.
+int32_t ring_chunks(int32_t B, int32_t Hkv, int32_t max_ctx, int waves_per_cu) {
+  return stream_chunks(B, Hkv, max_ctx, waves_per_cu, kRingChunkTiles, waves_per_cu);
 }
 
 // Balanced-mode workspace: m [S][G], l [S][G], o [S][G][d], prefix [B + 1] (int32) and
@@ -294,7 +298,7 @@ size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d_
   const int32_t ps = pkv_decode_partition_size(B, Hkv, max_context_len, partition_size);
   if (ps < 0 || Hq <= 0 || d_v <= 0 || Hq % Hkv) return 0;
   if (ps == 0) {
-    const int32_t chunks = ring_chunks(B, Hkv, max_context_len);
+    const int32_t chunks = ring_chunks(B, Hkv, max_context_len, kRingMaxWavesPerCu);
     return chunks < 0 ? 0 : stream_ws_bytes(B, Hq, Hkv, d_v, chunks);
   }
   return ws_bytes(B, Hq, d_v, num_parts(max_context_len, ps));
@@ -333,7 +337,7 @@ pkv_status pkv_paged_decode_attn(float* out, const void* q, const void* k_pool,
   if (ps < 0) return PKV_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
   if (ps == 0) {  // balanced mode
-    const int32_t chunks = ring_chunks(B, Hkv, ctx);
+    const int32_t chunks = ring_chunks(B, Hkv, ctx, pkv::ring_waves_per_cu(d, G, fp8));
     if (chunks < 0) return PKV_ERR_SHAPE;
     const size_t need = stream_ws_bytes(B, Hq, Hkv, d, chunks);
     if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;

@@ -67,6 +67,8 @@ struct DecodeArgs {
 hipError_t launch_gqa_decode(const DecodeArgs& a, hipStream_t s);
 // Balanced mode: decode kernel + merge kernel (always both).
 hipError_t launch_gqa_stream(const DecodeArgs& a, hipStream_t s);
+// Waves per CU (one workgroup per CU) of the balanced single-token decode kernel.
+int ring_waves_per_cu(int d, int G, bool fp8);
 // Merge of balanced-mode pieces for d_v = D (128, 64 or 512); reads a.ws_* and a.ws_prefix.
 hipError_t launch_stream_merge(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_partition_merge(const float* ws_m, const float* ws_l, const float* ws_o,

@@ -114,12 +114,14 @@ def test_partition_and_workspace_sizing(lib):
     assert lib.pkv_decode_partition_size(1, 8, 100, 20) < 0
 
 
-def _stream_chunks(B, Hkv, ctx, cus, waves_per_cu=4, max_tiles=256):
-    """One chunk per wave (the decode kernel runs one wave per SIMD: 4 per CU), at most the
-    bound on the tiles, at most 256 tiles each, a multiple of 32."""
+def _stream_chunks(B, Hkv, ctx, cus, waves_per_cu=8, max_tiles=512):
+    """One chunk per wave (the workspace query sizes for the decode kernel's larger shape, 8
+    waves per CU in 8-wave workgroups), at most the bound on the tiles, at most 512 tiles
+    each, a whole number of workgroups on each of the 8 XCDs."""
     tmax = Hkv * B * ((ctx + 15) // 16)
     c = max(min(waves_per_cu * cus, tmax), -(-tmax // max_tiles))
-    return max(32, -(-c // 32) * 32)
+    unit = 8 * waves_per_cu
+    return max(unit, -(-c // unit) * unit)
 
 
 def test_balanced_mode_workspace_size(lib):
