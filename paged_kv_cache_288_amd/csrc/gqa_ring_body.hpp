@@ -1,10 +1,11 @@
 // Balanced single-token GQA decode with an LDS ring (the body of gqa_stream_kernel).
 //
 // Division of work as in gqa_stream_body.hpp: the 16-token tiles of all (KV head, sequence)
-// segments laid end to end, head-major, cut into `chunks` equal ranges, one per wave, and a
-// piece of (m, l, o) partials written wherever a range meets a segment.  What differs is
-// how a wave is fed.  One 4-wave workgroup runs per CU, so every SIMD holds exactly one
-// wave and no wave waits behind another for its loads.  Each wave streams its range
+// segments laid end to end, head-major, cut into `chunks` ranges, one per wave, and a
+// piece of (m, l, o) partials written wherever a range meets a segment.  For large calls
+// the ranges are weighted by XCD (ring_chunk_start).  What differs is how a wave is fed.
+// One workgroup runs per CU, of 4 waves (one per SIMD, so no wave waits behind another for
+// its loads) or, for light tiles, 8 waves (two per SIMD).  Each wave streams its range
 // through a ring of kRing tile slots in LDS, filled by buffer loads that write LDS directly
 // (no registers): the K and V rows of tile n + kRing are requested as soon as tile n has
 // been read out of its slot, whether or not n + kRing belongs to the same piece.  The q rows
@@ -26,6 +27,37 @@ constexpr int kRingWaves = 4;      // waves per workgroup, one workgroup per CU 
 constexpr int kRingTilesPerLane = 8;
 constexpr int kRingMaxChunkTiles = kWave * kRingTilesPerLane;  // 512
 constexpr int kRingMaxSeqs = 4096;
+
+// Weighted ranges.  On MI355X the odd-numbered XCDs were measured to stream this kernel
+// about 6 % slower than the even ones (their waves finished 15-20 us later on a 200 us
+// call, on every box measured), and workgroup i runs on XCD i mod 8.  A wave's chunk is
+// (XCD) * C/8 + (workgroup within that XCD's share) * WPG + wave, so each XCD owns C/8
+// consecutive chunks; when every chunk holds at least kRingWeightMinTiles tiles on average,
+// the chunks of even XCDs take 17 parts of the tiles for the odd ones' 15 (with fewer, as
+// for a few 32K-token sequences, it was measured to cost more than it saved).  Only in the
+// 4-wave shape, whose heavy tiles stream from HBM: the 8-wave shape serves groups whose
+// tiles are light, where a shared prefix re-read from each XCD's own L2 sets the pace.  W(c) counts
+// the parts of chunks 0..c-1; chunk c covers tiles [T W(c) / 16C, T W(c+1) / 16C).
+// Unweighted, W(c) = 16 c, the equal split of gqa_stream_body.hpp.
+constexpr int kRingWeightMinTiles = 128;
+constexpr int kRingWeightEven = 17, kRingWeightOdd = 15;  // parts per chunk; sum 2 x 16
+
+__device__ __forceinline__ long long ring_chunk_start(int c, long long T, int C, bool wtd) {
+  if (!wtd) return T * c / C;
+  const int E = C / 8, x = c / E, r = c - x * E;
+  const long long W = (long long)E * (kRingWeightEven * ((x + 1) >> 1) + kRingWeightOdd * (x >> 1)) +
+                      (long long)r * ((x & 1) ? kRingWeightOdd : kRingWeightEven);
+  return T * W / (16LL * C);
+}
+// The chunk holding tile t (0 <= t < T): the last c with ring_chunk_start(c) <= t.
+__device__ __forceinline__ int ring_chunk_of(long long t, long long T, int C, bool wtd) {
+  if (!wtd) return chunk_of(t, T, C);
+  const long long E = C / 8;
+  const long long ws = ((t + 1) * 16LL * C - 1) / T;  // largest W(c) that still starts <= t
+  const long long pair = ws / (32 * E), rem = ws - pair * 32 * E;
+  if (rem < kRingWeightEven * E) return (int)(2 * pair * E + rem / kRingWeightEven);
+  return (int)((2 * pair + 1) * E + (rem - kRingWeightEven * E) / kRingWeightOdd);
+}
 
 typedef __attribute__((ext_vector_type(4))) int i32x4_t;
 typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
@@ -171,17 +203,30 @@ __device__ __forceinline__ void gqa_ring_body(const DecodeArgs& a, int bid, lds_
   }
   if (tid == NT - 1) s_pre[B] = run;
   __syncthreads();
-  if (bid == 0) {
-    for (int i = tid; i <= B; i += NT) a.ws_prefix[i] = s_pre[i];
-    write_segment_ranges(a.ws_seg, s_pre, B, a.Hkv, a.chunks, tid, NT);
-  }
-
-  // ---- this wave's chunk and, per lane, kRingTilesPerLane tiles' offset, length, segment
   const int T_head = __builtin_amdgcn_readfirstlane(s_pre[B]);
   const long long T = (long long)a.Hkv * T_head;
   const int C = a.chunks;
+  const bool wtd = WPG == 4 && T >= (long long)kRingWeightMinTiles * C;
+  if (bid == 0) {
+    // per segment: first chunk and chunks spanned, for the merge
+    for (int i = tid; i <= B; i += NT) a.ws_prefix[i] = s_pre[i];
+    for (int sg = tid; sg < a.Hkv * B; sg += NT) {
+      const int g = sg / B, b = sg - g * B;
+      const int nb = s_pre[b + 1] - s_pre[b];
+      int c0 = 0, n = 0;
+      if (nb > 0) {
+        const long long first = (long long)g * T_head + s_pre[b];
+        c0 = ring_chunk_of(first, T, C, wtd);
+        n = ring_chunk_of(first + nb - 1, T, C, wtd) - c0 + 1;
+      }
+      a.ws_seg[2 * sg] = c0;
+      a.ws_seg[2 * sg + 1] = n;
+    }
+  }
+
+  // ---- this wave's chunk and, per lane, kRingTilesPerLane tiles' offset, length, segment
   const int ch = (bid & 7) * (C / 8) + (bid >> 3) * WPG + w;
-  const long long tb = T * ch / C, te = T * (ch + 1) / C;
+  const long long tb = ring_chunk_start(ch, T, C, wtd), te = ring_chunk_start(ch + 1, T, C, wtd);
   const int ntl = (int)min(te - tb, (long long)kRingMaxChunkTiles);
 
   const int tiles_per_block = a.block_size / kTile;

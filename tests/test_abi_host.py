@@ -114,9 +114,9 @@ def test_partition_and_workspace_sizing(lib):
     assert lib.pkv_decode_partition_size(1, 8, 100, 20) < 0
 
 
-def _stream_chunks(B, Hkv, ctx, cus, waves_per_cu=8, max_tiles=512):
+def _stream_chunks(B, Hkv, ctx, cus, waves_per_cu=8, max_tiles=480):
     """One chunk per wave (the workspace query sizes for the decode kernel's larger shape, 8
-    waves per CU in 8-wave workgroups), at most the bound on the tiles, at most 512 tiles
+    waves per CU in 8-wave workgroups), at most the bound on the tiles, at most 480 tiles
     each, a whole number of workgroups on each of the 8 XCDs."""
     tmax = Hkv * B * ((ctx + 15) // 16)
     c = max(min(waves_per_cu * cus, tmax), -(-tmax // max_tiles))
@@ -170,6 +170,48 @@ def test_balanced_mode_piece_slots(lens, Hkv, C):
         c0, c1 = chunk_of(s0, T, C), chunk_of(s0 + nt[b] - 1, T, C)
         live = {c for c in range(c0, c1 + 1) if T * c // C != T * (c + 1) // C}
         assert chunks == live   # the merge reads exactly these pieces
+
+
+def _ring_chunk_start(c, T, C, wtd):
+    if not wtd:
+        return T * c // C
+    E = C // 8
+    x, r = divmod(c, E)
+    W = E * (17 * ((x + 1) // 2) + 15 * (x // 2)) + r * (15 if x & 1 else 17)
+    return T * W // (16 * C)
+
+
+def _ring_chunk_of(t, T, C, wtd):
+    if not wtd:
+        return chunk_of(t, T, C)
+    E = C // 8
+    ws = ((t + 1) * 16 * C - 1) // T
+    pair, rem = divmod(ws, 32 * E)
+    if rem < 17 * E:
+        return 2 * pair * E + rem // 17
+    return (2 * pair + 1) * E + (rem - 17 * E) // 15
+
+
+@pytest.mark.parametrize("T,C", [(128 * 64, 64), (70001, 64), (262144, 1024), (480 * 1024, 1024),
+                                 (159952, 1024), (99991, 512)])
+def test_ring_weighted_chunks(T, C):
+    """Host mirror of the decode kernel's XCD-weighted ranges: they tile [0, T) in order, the
+    inverse used for the merge's bookkeeping names the range that holds each tile, chunks of
+    even XCDs hold about 17/15 of the odd ones' tiles, and at the chunk count's bound of
+    480 tiles per chunk no range exceeds the 512 tiles a wave's tables hold."""
+    starts = [_ring_chunk_start(c, T, C, True) for c in range(C + 1)]
+    assert starts[0] == 0 and starts[-1] == T
+    assert all(b > a for a, b in zip(starts, starts[1:]))   # every chunk non-empty
+    if T <= 480 * C:   # the chunk count keeps T within this bound
+        assert max(b - a for a, b in zip(starts, starts[1:])) <= 512
+    E = C // 8
+    size = [starts[c + 1] - starts[c] for c in range(C)]
+    even = sum(size[c] for c in range(C) if (c // E) % 2 == 0)
+    assert abs(even / (T - even) - 17 / 15) < 0.01
+    step = max(1, T // 20000)
+    for t in list(range(0, T, step)) + [s for s in starts[1:-1]] + [s - 1 for s in starts[1:]]:
+        c = _ring_chunk_of(t, T, C, True)
+        assert starts[c] <= t < starts[c + 1], (t, c)
 
 
 def test_mla_rejects_bad_arguments_before_launch(lib):
