@@ -6,11 +6,11 @@
 // the ranges are weighted by XCD (ring_chunk_start).  What differs is how a wave is fed.
 // One workgroup runs per CU, of 4 waves (one per SIMD, so no wave waits behind another for
 // its loads) or, for light tiles, 8 waves (two per SIMD).  Each wave streams its range
-// through a ring of kRing tile slots in LDS, filled by buffer loads that write LDS directly
-// (no registers): the K and V rows of tile n + kRing are requested as soon as tile n has
-// been read out of its slot, whether or not n + kRing belongs to the same piece.  The q rows
+// through a ring of NS tile slots in LDS, filled by buffer loads that write LDS directly
+// (no registers): the K and V rows of tile n + NS are requested as soon as tile n has
+// been read out of its slot, whether or not n + NS belongs to the same piece.  The q rows
 // of a piece are copied the same way, just before the piece's first tile, into one of
-// kRing q slots, so a piece boundary never drains the loads in flight.  The arithmetic of a
+// NS q slots, so a piece boundary never drains the loads in flight.  The arithmetic of a
 // tile (scores, online softmax, p.V, merge of row groups) is that of gqa_tile.hpp.
 //
 // Reading the pages: "GPU推理深度拆解：KV Cache视角", section "性能指标与瓶颈" (decode is bound by
@@ -22,7 +22,7 @@
 
 namespace pkv {
 
-constexpr int kRing = 3;           // tiles in flight per wave (default)
+constexpr int kRing = 2;           // tiles in flight per wave (default)
 constexpr int kRingWaves = 4;      // waves per workgroup, one workgroup per CU (default)
 constexpr int kRingTilesPerLane = 8;
 constexpr int kRingMaxChunkTiles = kWave * kRingTilesPerLane;  // 512
@@ -93,7 +93,7 @@ __device__ __forceinline__ void ring_copy16(i32x4_t rsrc, uint32_t voff, uint32_
 }
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
-// LDS layout of one wave's ring: kRing slots of [K tile | V tile], then kRing q slots.
+// LDS layout of one wave's ring: NS slots of [K tile | V tile], then NS q slots.
 // Inside a slot the K rows of 256 bytes (bf16, d = 128) have their two 128-byte halves
 // swapped on odd tokens, and the V rows of 128 bytes (FP8, d = 128) are stored at row
 // t ^ ((t >> 1) & 1): with those, every 16-lane group of the K reads and every 32-lane

@@ -136,15 +136,16 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void stream_merge_kernel(Decod
 }
 
 // The library's default single-token decode: one workgroup per CU, each wave streaming its
-// chunk through an LDS ring (gqa_ring_body.hpp).  With 8 query heads per KV head a tile's
-// arithmetic keeps one wave busy while three tiles are in flight: 4 waves (one per SIMD)
-// with 3-tile rings, up to 512 registers each.  Smaller groups have lighter tiles, whose
-// arithmetic a single wave cannot hide when their data comes from L2 (a shared prefix
-// re-read): there two waves per SIMD, 2-tile rings, hide each other's arithmetic.
+// chunk through an LDS ring (gqa_ring_body.hpp) of 2 tiles (3 measured 0.7 % slower on
+// the 70B-shaped batch, 4 no faster).  With 8 query heads per KV head a tile's arithmetic
+// keeps one wave busy while its next tile is in flight: 4 waves (one per SIMD), up to 512
+// registers each.  Smaller groups have lighter tiles, whose arithmetic a single wave cannot
+// hide when their data comes from L2 (a shared prefix re-read): there two waves per SIMD
+// hide each other's arithmetic.
 template <int D, int G, bool FP8>
 struct RingShape {
   static constexpr int WPG = G == 8 ? 4 : 8;
-  static constexpr int NS = WPG == 4 ? 3 : 2;
+  static constexpr int NS = 2;
 };
 int ring_waves_per_cu(int d, int G, bool fp8) {
   (void)d;
