@@ -3,7 +3,7 @@
 // Division of work as in gqa_stream_body.hpp: the 16-token tiles of all (KV head, sequence)
 // segments laid end to end, head-major, cut into `chunks` ranges, one per wave, and a
 // piece of (m, l, o) partials written wherever a range meets a segment.  For large calls
-// the ranges are weighted by XCD (ring_chunk_start).  What differs is how a wave is fed.
+// the ranges are weighted by XCD (xcd_chunk_start).  What differs is how a wave is fed.
 // One workgroup runs per CU, of 4 waves (one per SIMD, so no wave waits behind another for
 // its loads) or, for light tiles, 8 waves (two per SIMD).  Each wave streams its range
 // through a ring of NS tile slots in LDS, filled by buffer loads that write LDS directly
@@ -28,36 +28,12 @@ constexpr int kRingTilesPerLane = 8;
 constexpr int kRingMaxChunkTiles = kWave * kRingTilesPerLane;  // 512
 constexpr int kRingMaxSeqs = 4096;
 
-// Weighted ranges.  On MI355X the odd-numbered XCDs were measured to stream this kernel
-// about 6 % slower than the even ones (their waves finished 15-20 us later on a 200 us
-// call, on every box measured), and workgroup i runs on XCD i mod 8.  A wave's chunk is
-// (XCD) * C/8 + (workgroup within that XCD's share) * WPG + wave, so each XCD owns C/8
-// consecutive chunks; when every chunk holds at least kRingWeightMinTiles tiles on average,
-// the chunks of even XCDs take 17 parts of the tiles for the odd ones' 15 (with fewer, as
-// for a few 32K-token sequences, it was measured to cost more than it saved).  Only in the
-// 4-wave shape, whose heavy tiles stream from HBM: the 8-wave shape serves groups whose
-// tiles are light, where a shared prefix re-read from each XCD's own L2 sets the pace.  W(c) counts
-// the parts of chunks 0..c-1; chunk c covers tiles [T W(c) / 16C, T W(c+1) / 16C).
-// Unweighted, W(c) = 16 c, the equal split of gqa_stream_body.hpp.
+// Ranges weighted by XCD (xcd_chunk_start in pkv_device.hpp) when the 4-wave shape's
+// chunks hold at least kRingWeightMinTiles tiles on average (with fewer, as for a few
+// 32K-token sequences, the weighting was measured to cost more than it saved).  Only in
+// the 4-wave shape, whose heavy tiles stream from HBM: the 8-wave shape serves groups whose
+// tiles are light, where a shared prefix re-read from each XCD's own L2 sets the pace.
 constexpr int kRingWeightMinTiles = 128;
-constexpr int kRingWeightEven = 17, kRingWeightOdd = 15;  // parts per chunk; sum 2 x 16
-
-__device__ __forceinline__ long long ring_chunk_start(int c, long long T, int C, bool wtd) {
-  if (!wtd) return T * c / C;
-  const int E = C / 8, x = c / E, r = c - x * E;
-  const long long W = (long long)E * (kRingWeightEven * ((x + 1) >> 1) + kRingWeightOdd * (x >> 1)) +
-                      (long long)r * ((x & 1) ? kRingWeightOdd : kRingWeightEven);
-  return T * W / (16LL * C);
-}
-// The chunk holding tile t (0 <= t < T): the last c with ring_chunk_start(c) <= t.
-__device__ __forceinline__ int ring_chunk_of(long long t, long long T, int C, bool wtd) {
-  if (!wtd) return chunk_of(t, T, C);
-  const long long E = C / 8;
-  const long long ws = ((t + 1) * 16LL * C - 1) / T;  // largest W(c) that still starts <= t
-  const long long pair = ws / (32 * E), rem = ws - pair * 32 * E;
-  if (rem < kRingWeightEven * E) return (int)(2 * pair * E + rem / kRingWeightEven);
-  return (int)((2 * pair + 1) * E + (rem - kRingWeightEven * E) / kRingWeightOdd);
-}
 
 typedef __attribute__((ext_vector_type(4))) int i32x4_t;
 typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
@@ -206,27 +182,15 @@ __device__ __forceinline__ void gqa_ring_body(const DecodeArgs& a, int bid, lds_
   const int T_head = __builtin_amdgcn_readfirstlane(s_pre[B]);
   const long long T = (long long)a.Hkv * T_head;
   const int C = a.chunks;
-  const bool wtd = WPG == 4 && T >= (long long)kRingWeightMinTiles * C;
+  const bool wtd = WPG == 4 && xcd_weighted(T, C, kRingWeightMinTiles, kRingMaxChunkTiles);
   if (bid == 0) {
-    // per segment: first chunk and chunks spanned, for the merge
     for (int i = tid; i <= B; i += NT) a.ws_prefix[i] = s_pre[i];
-    for (int sg = tid; sg < a.Hkv * B; sg += NT) {
-      const int g = sg / B, b = sg - g * B;
-      const int nb = s_pre[b + 1] - s_pre[b];
-      int c0 = 0, n = 0;
-      if (nb > 0) {
-        const long long first = (long long)g * T_head + s_pre[b];
-        c0 = ring_chunk_of(first, T, C, wtd);
-        n = ring_chunk_of(first + nb - 1, T, C, wtd) - c0 + 1;
-      }
-      a.ws_seg[2 * sg] = c0;
-      a.ws_seg[2 * sg + 1] = n;
-    }
+    write_segment_ranges_xcd(a.ws_seg, s_pre, B, a.Hkv, C, wtd, tid, NT);
   }
 
   // ---- this wave's chunk and, per lane, kRingTilesPerLane tiles' offset, length, segment
   const int ch = (bid & 7) * (C / 8) + (bid >> 3) * WPG + w;
-  const long long tb = ring_chunk_start(ch, T, C, wtd), te = ring_chunk_start(ch + 1, T, C, wtd);
+  const long long tb = xcd_chunk_start(ch, T, C, wtd), te = xcd_chunk_start(ch + 1, T, C, wtd);
   const int ntl = (int)min(te - tb, (long long)kRingMaxChunkTiles);
 
   const int tiles_per_block = a.block_size / kTile;

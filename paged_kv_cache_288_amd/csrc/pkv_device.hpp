@@ -172,4 +172,58 @@ __device__ __forceinline__ void write_segment_ranges(int32_t* ws_seg, PRE pre, i
   }
 }
 
+// ---- XCD-weighted ranges.  On MI355X the odd-numbered XCDs were measured to stream the
+// single-token decode 6-10 % slower than the even ones on most boxes (their waves finished
+// 15-20 us later on a 200 us call), and workgroup i runs on XCD i mod 8.  The balanced
+// kernels give wave w of workgroup i the chunk (i mod 8) * C/8 + (i / 8) * waves + w, so
+// each XCD owns C/8 consecutive chunks.  (The multi-token kernel, at 8 waves per CU and
+// about 74 tiles per chunk on the 70B-shaped verify batch, measured 2.6 % slower
+// weighted, and splits evenly.)  Weighted, the chunks of even XCDs take 17
+// parts of the tiles for the odd ones' 15: W(c) counts the parts of chunks 0 .. c-1, and
+// chunk c covers tiles [T W(c) / 16C, T W(c+1) / 16C).  Unweighted, W(c) = 16 c: the equal
+// split above.
+constexpr int kXcdWeightEven = 17, kXcdWeightOdd = 15;  // parts per chunk; sum 2 x 16
+
+__device__ __forceinline__ long long xcd_chunk_start(int c, long long T, int C, bool wtd) {
+  if (!wtd) return T * c / C;
+  const int E = C / 8, x = c / E, r = c - x * E;
+  const long long W = (long long)E * (kXcdWeightEven * ((x + 1) >> 1) + kXcdWeightOdd * (x >> 1)) +
+                      (long long)r * ((x & 1) ? kXcdWeightOdd : kXcdWeightEven);
+  return T * W / (16LL * C);
+}
+// The chunk holding tile t (0 <= t < T): the last c with xcd_chunk_start(c) <= t.
+__device__ __forceinline__ int xcd_chunk_of(long long t, long long T, int C, bool wtd) {
+  if (!wtd) return chunk_of(t, T, C);
+  const long long E = C / 8;
+  const long long ws = ((t + 1) * 16LL * C - 1) / T;  // largest W(c) that still starts <= t
+  const long long pair = ws / (32 * E), rem = ws - pair * 32 * E;
+  if (rem < kXcdWeightEven * E) return (int)(2 * pair * E + rem / kXcdWeightEven);
+  return (int)((2 * pair + 1) * E + (rem - kXcdWeightEven * E) / kXcdWeightOdd);
+}
+// Whether to weight: chunks hold at least min_tiles tiles on average (below that the
+// weighting was measured to cost more than it saved), and the heavier chunks, up to
+// T * 17 / 16C + 1 tiles, still fit a wave's max_tiles.
+__device__ __forceinline__ bool xcd_weighted(long long T, int C, int min_tiles, int max_tiles) {
+  return T >= (long long)min_tiles * C && kXcdWeightEven * T <= 16LL * C * (max_tiles - 1);
+}
+// write_segment_ranges over the (possibly weighted) ranges.
+template <typename PRE>
+__device__ __forceinline__ void write_segment_ranges_xcd(int32_t* ws_seg, PRE pre, int B, int H,
+                                                         int C, bool wtd, int tid, int nthreads) {
+  const int T_head = pre[B];
+  const long long T = (long long)H * T_head;
+  for (int sg = tid; sg < H * B; sg += nthreads) {
+    const int g = sg / B, b = sg - g * B;
+    const int nb = pre[b + 1] - pre[b];
+    int c0 = 0, n = 0;
+    if (nb > 0) {
+      const long long first = (long long)g * T_head + pre[b];
+      c0 = xcd_chunk_of(first, T, C, wtd);
+      n = xcd_chunk_of(first + nb - 1, T, C, wtd) - c0 + 1;
+    }
+    ws_seg[2 * sg] = c0;
+    ws_seg[2 * sg + 1] = n;
+  }
+}
+
 }  // namespace pkv

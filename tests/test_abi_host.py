@@ -172,7 +172,7 @@ def test_balanced_mode_piece_slots(lens, Hkv, C):
         assert chunks == live   # the merge reads exactly these pieces
 
 
-def _ring_chunk_start(c, T, C, wtd):
+def _xcd_chunk_start(c, T, C, wtd):
     if not wtd:
         return T * c // C
     E = C // 8
@@ -181,7 +181,7 @@ def _ring_chunk_start(c, T, C, wtd):
     return T * W // (16 * C)
 
 
-def _ring_chunk_of(t, T, C, wtd):
+def _xcd_chunk_of(t, T, C, wtd):
     if not wtd:
         return chunk_of(t, T, C)
     E = C // 8
@@ -192,14 +192,23 @@ def _ring_chunk_of(t, T, C, wtd):
     return (2 * pair + 1) * E + (rem - 17 * E) // 15
 
 
+def _xcd_weighted(T, C, min_tiles, max_tiles):
+    return T >= min_tiles * C and 17 * T <= 16 * C * (max_tiles - 1)
+
+
 @pytest.mark.parametrize("T,C", [(128 * 64, 64), (70001, 64), (262144, 1024), (480 * 1024, 1024),
-                                 (159952, 1024), (99991, 512)])
-def test_ring_weighted_chunks(T, C):
-    """Host mirror of the decode kernel's XCD-weighted ranges: they tile [0, T) in order, the
-    inverse used for the merge's bookkeeping names the range that holds each tile, chunks of
-    even XCDs hold about 17/15 of the odd ones' tiles, and at the chunk count's bound of
-    480 tiles per chunk no range exceeds the 512 tiles a wave's tables hold."""
-    starts = [_ring_chunk_start(c, T, C, True) for c in range(C + 1)]
+                                 (159952, 1024), (99991, 512), (152000, 2048), (2048 * 119, 2048)])
+def test_xcd_weighted_chunks(T, C):
+    """Host mirror of the balanced kernels' XCD-weighted ranges: they tile [0, T) in order,
+    the inverse used for the merge's bookkeeping names the range that holds each tile,
+    chunks of even XCDs hold about 17/15 of the odd ones' tiles, and whenever the weighting
+    is switched on (512 tiles per wave, chunk counts for 480) no range exceeds what a wave's
+    tables hold."""
+    for max_tiles in (512, 128):
+        if _xcd_weighted(T, C, 64, max_tiles):
+            starts = [_xcd_chunk_start(c, T, C, True) for c in range(C + 1)]
+            assert max(b - a for a, b in zip(starts, starts[1:])) <= max_tiles
+    starts = [_xcd_chunk_start(c, T, C, True) for c in range(C + 1)]
     assert starts[0] == 0 and starts[-1] == T
     assert all(b > a for a, b in zip(starts, starts[1:]))   # every chunk non-empty
     if T <= 480 * C:   # the chunk count keeps T within this bound
@@ -210,7 +219,7 @@ def test_ring_weighted_chunks(T, C):
     assert abs(even / (T - even) - 17 / 15) < 0.01
     step = max(1, T // 20000)
     for t in list(range(0, T, step)) + [s for s in starts[1:-1]] + [s - 1 for s in starts[1:]]:
-        c = _ring_chunk_of(t, T, C, True)
+        c = _xcd_chunk_of(t, T, C, True)
         assert starts[c] <= t < starts[c + 1], (t, c)
 
 
