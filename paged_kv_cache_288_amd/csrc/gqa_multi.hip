@@ -30,9 +30,25 @@
 // (KV head, sequence) segments laid end to end, cut into equal ranges, one per wave; each
 // range yields one (m, l, o) piece per segment it meets, and multi_merge_kernel combines
 // the pieces of each segment.
-#include "gqa_multi_body.hpp"
+//
+// Two kernels do this.  For bf16 K/V of 128 dims and up to 32 rows, gqa_multi_ring_kernel
+// streams K, V and q through an LDS ring (gqa_multi_ring_body.hpp), one wave per SIMD;
+// otherwise (FP8, 64 dims, 64 rows, the cascade's prefix role) gqa_multi_kernel holds its
+// tiles in registers, two waves per SIMD (gqa_multi_body.hpp).
+#include "gqa_multi_ring_body.hpp"
 
 namespace pkv {
+
+template <int RT>
+__global__ __launch_bounds__(kRingWaves * kWave, 1) void gqa_multi_ring_kernel(MultiArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t s_lds[multi_ring_lds_bytes<RT>()];
+  gqa_multi_ring_body<RT>(a, blockIdx.x, (lds_u8_t*)s_lds);
+}
+
+// The ring kernel serves bf16 K/V, d = 128, up to 32 rows, every q row its own (not the
+// cascade's prefix mode).
+bool multi_uses_ring(int d, int rows, bool fp8) { return d == 128 && rows <= 32 && !fp8; }
+int multi_ring_waves_per_cu() { return kRingWaves; }
 
 template <int D, int RT, bool FP8>
 __global__ __launch_bounds__(kMW * kWave, multi_waves_per_simd(D, RT)) void gqa_multi_kernel(MultiArgs a) {
@@ -156,7 +172,21 @@ __global__ __launch_bounds__(kMultiMergeWaves * kWave) void multi_merge_kernel(M
 
 template <int D, int RT, bool FP8>
 static hipError_t launch_multi_one(const MultiArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((gqa_multi_kernel<D, RT, FP8>), dim3(a.chunks / kMW), dim3(kMW * kWave), 0, s, a);
+  const int R = a.Hq / a.Hkv * a.q_len;
+  if (multi_uses_ring(D, R, FP8)) {  // chunks were sized for it (up to 480 tiles each)
+    if constexpr (D == 128 && RT <= 2 && !FP8) {
+      // chunk = (XCD eighth) + (workgroup within it) * 4 + wave: whole workgroups per eighth
+      if (a.chunks % (8 * kRingWaves) || a.B > kRingMaxSeqs || a.q_rows != a.B * a.q_len ||
+          a.fixed_len >= 0)
+        return hipErrorInvalidValue;
+      hipLaunchKernelGGL((gqa_multi_ring_kernel<RT>), dim3(a.chunks / kRingWaves),
+                         dim3(kRingWaves * kWave), 0, s, a);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else {
+    hipLaunchKernelGGL((gqa_multi_kernel<D, RT, FP8>), dim3(a.chunks / kMW), dim3(kMW * kWave), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)(((long long)a.B * a.q_len * a.Hkv + kMultiMergeWaves - 1) / kMultiMergeWaves));

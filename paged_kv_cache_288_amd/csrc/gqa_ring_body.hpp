@@ -128,21 +128,41 @@ __device__ __forceinline__ void wait_vm_dyn(int k) {
   wait_vm<BASE>();
 }
 
-template <int D, int G, bool FP8, int NS = kRing, int WPG = kRingWaves>
-__device__ __forceinline__ void gqa_ring_body(const DecodeArgs& a, int bid, lds_u8_t* lds) {
-  using Lo = Layout<D, FP8>;
-  using R = Ring<D, G, FP8, NS>;
-  static_assert(NS >= 2 && NS <= 4, "ring depth");
-  static_assert(WPG == 4 || WPG == 8, "waves per workgroup");
+// ---- set-up of a ring walk, common to the single- and the multi-token ring kernels
+struct RingWalk {
+  const int32_t* context_lens;  // per-sequence lengths, or nullptr: every sequence fixed_len
+  int fixed_len;
+  const int32_t* block_table;
+  size_t table_stride;          // elements between the rows of sequences (0: one shared row)
+  int B, Hkv, block_size, num_blocks;
+  int cap;                      // lengths are clamped to [0, cap]
+  int chunks;
+  int32_t* ws_prefix;           // written by workgroup 0: tile prefix [B + 1]
+  int32_t* ws_seg;              //   and per segment its first chunk and chunk count
+};
+// One wave's chunk: per lane, kRingTilesPerLane tiles (tile n of the chunk in entry n / 64 of
+// lane n % 64): byte offset / 256 of its first row in the pools, valid tokens | segment << 5,
+// and one bit per tile that opens a piece (its segment differs from the previous tile's).
+struct RingTiles {
+  uint32_t off[kRingTilesPerLane];
+  int info[kRingTilesPerLane];
+  int len[kRingTilesPerLane];  // length of the tile's sequence (clamped)
+  uint64_t starts[kRingTilesPerLane];
+  int ntl;       // tiles in the chunk
+  int ch;        // the chunk
+  int tt_first;  // index inside its sequence of the chunk's first tile
+};
+// Tiles per sequence and their exclusive prefix in LDS (which the ring aliases: the function
+// ends with a workgroup barrier after its last LDS read), this wave's chunk (XCD-weighted
+// when `may_weight` and the call is large), and the tables.  ROW = bytes per K or V row.
+template <int ROW, int WPG>
+__device__ __forceinline__ void ring_setup(const RingWalk& g, int bid, lds_u8_t* lds,
+                                           bool may_weight, RingTiles& t) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int k = lane >> 3, c = lane & 7, r = lane / Lo::LPT, dc = lane % Lo::LPT;
-  const int B = a.B;
-  const int cap = min(a.max_blocks * a.block_size, a.max_context_len);
+  const int B = g.B;
+  const int cap = g.cap;
   constexpr int NT = WPG * kWave;
-
-  // ---- tiles per sequence and their exclusive prefix (aliased with the ring: the ring is
-  // first written after the barrier that ends this part)
   __attribute__((address_space(3))) int* s_pre =
       (__attribute__((address_space(3))) int*)lds;        // [B + 1]
   __attribute__((address_space(3))) int* s_len = s_pre + (kRingMaxSeqs + 1);  // [B] lengths
@@ -152,7 +172,7 @@ __device__ __forceinline__ void gqa_ring_body(const DecodeArgs& a, int bid, lds_
   for (int i = 0; i < per; ++i) {
     const int bi = tid * per + i;
     if (bi < B) {
-      int L = a.context_lens[bi];
+      int L = g.context_lens ? g.context_lens[bi] : g.fixed_len;
       L = L < 0 ? 0 : (L > cap ? cap : L);
       s_len[bi] = L;
       local += (L + kTile - 1) / kTile;
@@ -180,24 +200,25 @@ __device__ __forceinline__ void gqa_ring_body(const DecodeArgs& a, int bid, lds_
   if (tid == NT - 1) s_pre[B] = run;
   __syncthreads();
   const int T_head = __builtin_amdgcn_readfirstlane(s_pre[B]);
-  const long long T = (long long)a.Hkv * T_head;
-  const int C = a.chunks;
-  const bool wtd = WPG == 4 && xcd_weighted(T, C, kRingWeightMinTiles, kRingMaxChunkTiles);
+  const long long T = (long long)g.Hkv * T_head;
+  const int C = g.chunks;
+  const bool wtd = may_weight && xcd_weighted(T, C, kRingWeightMinTiles, kRingMaxChunkTiles);
   if (bid == 0) {
-    for (int i = tid; i <= B; i += NT) a.ws_prefix[i] = s_pre[i];
-    write_segment_ranges_xcd(a.ws_seg, s_pre, B, a.Hkv, C, wtd, tid, NT);
+    for (int i = tid; i <= B; i += NT) g.ws_prefix[i] = s_pre[i];
+    write_segment_ranges_xcd(g.ws_seg, s_pre, B, g.Hkv, C, wtd, tid, NT);
   }
 
   // ---- this wave's chunk and, per lane, kRingTilesPerLane tiles' offset, length, segment
   const int ch = (bid & 7) * (C / 8) + (bid >> 3) * WPG + w;
   const long long tb = xcd_chunk_start(ch, T, C, wtd), te = xcd_chunk_start(ch + 1, T, C, wtd);
   const int ntl = (int)min(te - tb, (long long)kRingMaxChunkTiles);
+  t.ntl = ntl;
+  t.ch = ch;
 
-  const int tiles_per_block = a.block_size / kTile;
-  const size_t head_bytes = (size_t)a.block_size * Lo::ROW;
-  const size_t block_bytes = head_bytes * a.Hkv;
-  uint32_t off_l[kRingTilesPerLane];
-  int info_l[kRingTilesPerLane];  // valid tokens (5 bits) | segment << 5
+  const int tiles_per_block = g.block_size / kTile;
+  const size_t head_bytes = (size_t)g.block_size * ROW;
+  const size_t block_bytes = head_bytes * g.Hkv;
+  int tt_l = 0;
   {
     // head and tile-in-head of the lane's tiles: the chunk starts at head gg0, tile rem0 of
     // it, and a lane's tile lies fewer than kRingMaxChunkTiles tiles further
@@ -236,38 +257,61 @@ __device__ __forceinline__ void gqa_ring_body(const DecodeArgs& a, int bid, lds_
     }
 #pragma unroll
     for (int j = 0; j < kRingTilesPerLane; ++j) {
-      off_l[j] = 0;
-      info_l[j] = 0;
+      t.off[j] = 0;
+      t.info[j] = 0;
+      t.len[j] = 0;
       const int n = kWave * j + lane;
       if (n < ntl) {
         const int tt = rem_[j] - s_pre[lo_[j]];
+        if (j == 0) tt_l = tt;
         const int L = s_len[lo_[j]];
         const int blk = tiles_per_block == 1 ? tt : tt / tiles_per_block;
         const int tin = tiles_per_block == 1 ? 0 : tt - blk * tiles_per_block;
-        const int phys = a.block_table[(size_t)lo_[j] * a.max_blocks + blk];
-        const bool ok = (unsigned)phys < (unsigned)a.num_blocks;
+        const int phys = g.block_table[(size_t)lo_[j] * g.table_stride + blk];
+        const bool ok = (unsigned)phys < (unsigned)g.num_blocks;
         const uint64_t off = (uint64_t)(ok ? phys : 0) * block_bytes +
                              (uint64_t)gg_[j] * head_bytes +
-                             (uint64_t)tin * (kTile * Lo::ROW);
-        off_l[j] = (uint32_t)(off >> 8);
-        info_l[j] = (ok ? min(kTile, L - tt * kTile) : 0) | ((gg_[j] * B + lo_[j]) << 5);
+                             (uint64_t)tin * (kTile * ROW);
+        t.off[j] = (uint32_t)(off >> 8);
+        t.info[j] = (ok ? min(kTile, L - tt * kTile) : 0) | ((gg_[j] * B + lo_[j]) << 5);
+        t.len[j] = L;
       }
     }
   }
+  t.tt_first = __builtin_amdgcn_readlane(tt_l, 0);
   // the prefix area is reused by the ring from here on
   __syncthreads();
-  if (ntl <= 0) return;
 
-  // tiles that open a piece (segment differs from the previous tile's), one bit per tile
-  uint64_t starts[kRingTilesPerLane];
 #pragma unroll
   for (int j = 0; j < kRingTilesPerLane; ++j) {
     const int n = kWave * j + lane;
-    const int sg = info_l[j] >> 5;
+    const int sg = t.info[j] >> 5;
     int prev = __shfl_up(sg, 1);
-    if (lane == 0) prev = j ? __builtin_amdgcn_readlane(info_l[j - 1], kWave - 1) >> 5 : -1;
-    starts[j] = __builtin_amdgcn_ballot_w64(n < ntl && sg != prev);
+    if (lane == 0) prev = j ? __builtin_amdgcn_readlane(t.info[j - 1], kWave - 1) >> 5 : -1;
+    t.starts[j] = __builtin_amdgcn_ballot_w64(n < ntl && sg != prev);
   }
+}
+
+template <int D, int G, bool FP8, int NS = kRing, int WPG = kRingWaves>
+__device__ __forceinline__ void gqa_ring_body(const DecodeArgs& a, int bid, lds_u8_t* lds) {
+  using Lo = Layout<D, FP8>;
+  using R = Ring<D, G, FP8, NS>;
+  static_assert(NS >= 2 && NS <= 4, "ring depth");
+  static_assert(WPG == 4 || WPG == 8, "waves per workgroup");
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int k = lane >> 3, c = lane & 7, r = lane / Lo::LPT, dc = lane % Lo::LPT;
+  const int B = a.B;
+  const RingWalk gw{a.context_lens, 0, a.block_table, (size_t)a.max_blocks, B, a.Hkv, a.block_size,
+                    a.num_blocks, min(a.max_blocks * a.block_size, a.max_context_len), a.chunks,
+                    a.ws_prefix, a.ws_seg};
+  RingTiles tl;
+  ring_setup<Lo::ROW, WPG>(gw, bid, lds, WPG == 4, tl);
+  const int ntl = tl.ntl, ch = tl.ch;
+  if (ntl <= 0) return;
+  uint32_t (&off_l)[kRingTilesPerLane] = tl.off;
+  int (&info_l)[kRingTilesPerLane] = tl.info;
+  uint64_t (&starts)[kRingTilesPerLane] = tl.starts;
 
   // ---- LDS: this wave's ring and q slots; per-lane copy and read offsets
   lds_u8_t* const ring = lds + w * R::WAVE_BYTES;

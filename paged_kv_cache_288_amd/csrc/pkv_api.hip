@@ -188,8 +188,14 @@ size_t multi_ws_bytes(int32_t B, int32_t q_len, int32_t Hq, int32_t Hkv, int32_t
          round256((size_t)Hkv * B * 2 * sizeof(int32_t));
 }
 
+// The workspace query does not know the element type: it sizes for the register-tile
+// kernel (8 waves per CU, 128 tiles per wave), which never has fewer chunks than the ring
+// kernel (4 waves per CU, 480 tiles per wave).
 int32_t multi_chunks(int32_t B, int32_t q_len, int32_t Hq, int32_t Hkv, int32_t d,
-                     int32_t max_context_len) {
+                     int32_t max_context_len, bool ring) {
+  if (ring)
+    return stream_chunks(B, Hkv, max_context_len, pkv::multi_ring_waves_per_cu(), kRingChunkTiles,
+                         pkv::multi_ring_waves_per_cu());
   return stream_chunks(B, Hkv, max_context_len,
                        pkv::multi_waves_per_cu(d, (Hq / Hkv) * q_len));
 }
@@ -481,7 +487,7 @@ size_t pkv_multi_workspace_bytes(int32_t B, int32_t q_len, int32_t Hq, int32_t H
   if ((long long)G * q_len > 64 || (G != 1 && G != 2 && G != 4 && G != 8) ||
       (long long)Hkv * B >= (1LL << 26))
     return 0;
-  const int32_t chunks = multi_chunks(B, q_len, Hq, Hkv, d, max_context_len);
+  const int32_t chunks = multi_chunks(B, q_len, Hq, Hkv, d, max_context_len, false);
   return chunks < 0 ? 0 : multi_ws_bytes(B, q_len, Hq, Hkv, d, chunks);
 }
 
@@ -510,7 +516,8 @@ pkv_status pkv_paged_decode_attn_multi(float* out, const void* q, const void* k_
       (fp8 && (!aligned4(k_scale) || !aligned4(v_scale))))
     return PKV_ERR_ALIGN;
   if (B > kMaxStreamSeqs || (long long)Hkv * B >= (1LL << 26)) return PKV_ERR_SHAPE;
-  const int32_t chunks = multi_chunks(B, q_len, Hq, Hkv, d, max_context_len);
+  const int32_t chunks = multi_chunks(B, q_len, Hq, Hkv, d, max_context_len,
+                                      pkv::multi_uses_ring(d, G * q_len, fp8));
   if (chunks < 0) return PKV_ERR_SHAPE;
   if (!workspace || workspace_bytes < multi_ws_bytes(B, q_len, Hq, Hkv, d, chunks))
     return PKV_ERR_WORKSPACE;

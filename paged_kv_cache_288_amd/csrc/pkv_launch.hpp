@@ -150,6 +150,10 @@ struct MultiArgs {
 hipError_t launch_gqa_multi(const MultiArgs& a, hipStream_t s);
 // Resident waves per CU of the multi-token decode kernel for head dim d and q_len * G rows.
 int multi_waves_per_cu(int d, int rows);
+// Whether the multi-token call runs the LDS-ring kernel (then multi_ring_waves_per_cu()
+// waves per CU, up to 512 tiles per wave).
+bool multi_uses_ring(int d, int rows, bool fp8);
+int multi_ring_waves_per_cu();
 
 // Balanced-mode single-token decode kernel only (pieces for a later merge).
 hipError_t launch_gqa_stream_pieces(const DecodeArgs& a, hipStream_t s);
