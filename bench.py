@@ -49,6 +49,7 @@ KERNEL_SOURCES = {
             "paged_kv_cache_288_amd/csrc/gqa_stream_body.hpp", "paged_kv_cache_288_amd/csrc/gqa_tile.hpp",
             "paged_kv_cache_288_amd/csrc/pkv_device.hpp"],
     "multi": ["paged_kv_cache_288_amd/csrc/gqa_multi.hip", "paged_kv_cache_288_amd/csrc/gqa_multi_body.hpp",
+              "paged_kv_cache_288_amd/csrc/gqa_multi_ring_body.hpp", "paged_kv_cache_288_amd/csrc/gqa_ring_body.hpp",
               "paged_kv_cache_288_amd/csrc/gqa_tile.hpp", "paged_kv_cache_288_amd/csrc/pkv_device.hpp"],
     "cascade": ["paged_kv_cache_288_amd/csrc/gqa_cascade.hip", "paged_kv_cache_288_amd/csrc/gqa_stream_body.hpp",
                 "paged_kv_cache_288_amd/csrc/gqa_multi_body.hpp", "paged_kv_cache_288_amd/csrc/gqa_tile.hpp",
@@ -122,7 +123,9 @@ def kernel_label(w, pkv, ps, cascade=False):
         return ("pkv_paged_decode_attn_cascade call (cascade_kernel: tails and shared prefix "
                 "in one launch, then cascade_merge_kernel)")
     if w.q_len > 1:
-        return "pkv_paged_decode_attn_multi call (gqa_multi_kernel + multi_merge_kernel)"
+        ring = w.kv_dtype == "bf16" and w.d == 128 and (w.Hq // w.Hkv) * w.q_len <= 32
+        return ("pkv_paged_decode_attn_multi call (%s + multi_merge_kernel)"
+                % ("gqa_multi_ring_kernel" if ring else "gqa_multi_kernel"))
     if w.kind == "mla":
         if ps == 0 and w.Hq % 64 == 0 and w.Hq <= 128:
             return "pkv_paged_decode_attn_mla call, balanced mode (mla_split_kernel + stream_merge_kernel<512>)"
