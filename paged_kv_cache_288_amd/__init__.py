@@ -125,6 +125,25 @@ def _dtype_code(kv_dtype):
     return _DTYPES[kv_dtype]
 
 
+def _check_pools(k_pool, v_pool, kv_dtype, latent=False):
+    """The library trusts the pool geometry it is given; a pool whose element size differs
+    from kv_dtype's would be addressed past its end.  Reject such calls here, before any
+    launch: element size 2 for bf16, 1 for FP8 codes; [num_blocks, Hkv, block_size, d]
+    (latent: [num_blocks, block_size, d]); V shaped and typed like K."""
+    want = 1 if kv_dtype == "fp8" else 2
+    dims = 3 if latent else 4
+    for name, pool in (("k_pool", k_pool), ("v_pool", v_pool)):
+        if pool is None:
+            continue
+        if pool.dim() != dims:
+            raise ValueError(f"{name} must have {dims} dimensions, got shape {tuple(pool.shape)}")
+        if pool.element_size() != want:
+            raise ValueError(f"{name} has {pool.element_size()}-byte elements; kv_dtype "
+                             f"{kv_dtype!r} stores {want}-byte ones")
+    if v_pool is not None and tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError(f"v_pool shape {tuple(v_pool.shape)} differs from k_pool's {tuple(k_pool.shape)}")
+
+
 def abi_version():
     return load_library().pkv_abi_version()
 
@@ -138,6 +157,7 @@ def kv_append(k_pool, v_pool, k_new, v_new, slot_mapping, kv_dtype="bf16"):
     or torch.float8_e4m3fn) on the current device.
     """
     mla = v_pool is None
+    _check_pools(k_pool, v_pool, kv_dtype, latent=mla)
     if mla:
         num_blocks, bs, d = k_pool.shape
         Hkv = 1
@@ -176,6 +196,7 @@ def paged_decode_attn(out, q, k_pool, v_pool, block_table, context_lens, scale, 
     [B, max_blocks] int32; context_lens [B] int32; k_scale/v_scale [Hkv] fp32 for FP8.
     The workspace (device bytes) is allocated here with torch when not given.
     """
+    _check_pools(k_pool, v_pool, kv_dtype)
     B, Hq, d = q.shape
     num_blocks, Hkv, bs, _ = k_pool.shape
     lib = load_library()
@@ -196,6 +217,7 @@ def paged_decode_attn_noalloc(out, q, k_pool, v_pool, block_table, context_lens,
     """out[B, Hq, d] (fp32) = paged decode attention through pkv_paged_decode_attn_noalloc:
     the same computation as paged_decode_attn, with the library's device scratch
     (PKV_NOALLOC_SCRATCH_BYTES per GPU) as the workspace; nothing is allocated."""
+    _check_pools(k_pool, v_pool, kv_dtype)
     B, Hq, d = q.shape
     num_blocks, Hkv, bs, _ = k_pool.shape
     st = load_library().pkv_paged_decode_attn_noalloc(
@@ -217,6 +239,7 @@ def paged_decode_attn_mla(out, q, kv_pool, block_table, context_lens, scale, max
 
     q [B, Hq, d_qk] bf16; kv_pool [num_blocks, block_size, d_qk] bf16.
     """
+    _check_pools(kv_pool, None, "bf16", latent=True)
     B, Hq, d_qk = q.shape
     num_blocks, bs, _ = kv_pool.shape
     lib = load_library()
@@ -243,6 +266,7 @@ def paged_decode_attn_multi(out, q, k_pool, v_pool, block_table, context_lens, s
     q [B, q_len, Hq, d] bf16; pools [num_blocks, Hkv, block_size, d]; context_lens count
     the new tokens, whose K/V are already in the pools; k_scale/v_scale [Hkv] for FP8.
     """
+    _check_pools(k_pool, v_pool, kv_dtype)
     B, q_len, Hq, d = q.shape
     num_blocks, Hkv, bs, _ = k_pool.shape
     lib = load_library()
@@ -267,6 +291,7 @@ def paged_decode_attn_cascade(out, q, k_pool, v_pool, prefix_blocks, prefix_len,
     """out[B, Hq, d] (fp32) = decode attention over a shared prefix (prefix_blocks
     [prefix_len / block_size] int32) followed by each sequence's tail (tail_table
     [B, max_tail_blocks] int32, tail_lens [B] int32) (pkv_paged_decode_attn_cascade)."""
+    _check_pools(k_pool, v_pool, kv_dtype)
     B, Hq, d = q.shape
     num_blocks, Hkv, bs, _ = k_pool.shape
     lib = load_library()
@@ -295,6 +320,7 @@ def validate(block_table, context_lens, num_blocks, block_size, slot_mapping=Non
     T = 0 if slot_mapping is None else slot_mapping.shape[0]
     Hkv = d = 0
     if v_pool is not None:
+        _check_pools(v_pool, None, "bf16", latent=v_pool.dim() == 3)
         if v_pool.dim() == 3:
             Hkv, d = 1, v_pool.shape[2]
         else:
@@ -314,6 +340,7 @@ def kv_append_fp8(k_pool, v_pool, k_new, v_new, k_scale, v_scale, slot_mapping):
     """Quantizing append (pkv_kv_append_fp8): bf16 rows k_new/v_new [T, Hkv, d] stored as
     FP8 E4M3 codes of x / scale[h] into the uint8 pools [num_blocks, Hkv, block_size, d];
     k_scale/v_scale [Hkv] fp32.  v_pool/v_new/v_scale may be None (K only)."""
+    _check_pools(k_pool, v_pool, "fp8")
     num_blocks, Hkv, bs, d = k_pool.shape
     T = slot_mapping.shape[0]
     st = load_library().pkv_kv_append_fp8(
@@ -326,6 +353,7 @@ def kv_copy_blocks(k_pool, v_pool, src_blocks, dst_blocks, kv_dtype="bf16"):
     """Copy-on-write support (pkv_kv_copy_blocks): block dst[i] <- block src[i] in each pool.
     Pools [num_blocks, Hkv, block_size, d] (an MLA latent pool [num_blocks, block_size,
     d] with v_pool None); src/dst int32 device tensors [n]."""
+    _check_pools(k_pool, v_pool, kv_dtype, latent=k_pool.dim() == 3)
     if k_pool.dim() == 3:
         num_blocks, bs, d = k_pool.shape
         Hkv = 1

@@ -242,6 +242,7 @@ __device__ __forceinline__ void ring_setup(const RingWalk& g, int bid, lds_u8_t*
     int hi_[kRingTilesPerLane];
 #pragma unroll
     for (int j = 0; j < kRingTilesPerLane; ++j) hi_[j] = B - 1;
+#pragma unroll 1
     for (int step = 0; step < 13; ++step) {
       bool any = false;
 #pragma unroll

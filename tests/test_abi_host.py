@@ -242,6 +242,31 @@ def test_mla_rejects_bad_arguments_before_launch(lib):
     assert call(a12=8192, a14=64) == -6  # split without a workspace
 
 
+def test_binding_rejects_pools_that_do_not_match_kv_dtype():
+    """The library trusts the pool geometry it is given, so a pool whose element size
+    differs from kv_dtype's would be addressed past its end; the binding refuses such calls
+    before any launch (CPU tensors: nothing reaches the library)."""
+    torch = pytest.importorskip("torch")
+    q = torch.zeros((2, 8, 128), dtype=torch.int16)
+    out = torch.zeros((2, 8, 128), dtype=torch.float32)
+    bt = torch.zeros((2, 4), dtype=torch.int32)
+    cl = torch.zeros((2,), dtype=torch.int32)
+    fp8_pool = torch.zeros((10, 1, 16, 128), dtype=torch.uint8)
+    bf16_pool = torch.zeros((10, 1, 16, 128), dtype=torch.int16)
+    with pytest.raises(ValueError, match="1-byte elements"):
+        pkv.paged_decode_attn(out, q, fp8_pool, fp8_pool, bt, cl, 0.1, 64)        # FP8 pool as bf16
+    with pytest.raises(ValueError, match="2-byte elements"):
+        pkv.paged_decode_attn(out, q, bf16_pool, bf16_pool, bt, cl, 0.1, 64, kv_dtype="fp8")
+    with pytest.raises(ValueError, match="differs"):
+        pkv.paged_decode_attn(out, q, bf16_pool, bf16_pool[:5], bt, cl, 0.1, 64)
+    with pytest.raises(ValueError, match="dimensions"):
+        pkv.paged_decode_attn_mla(out, q, bf16_pool, bt, cl, 0.1, 64)            # latent pools are 3-D
+    with pytest.raises(ValueError, match="1-byte elements"):
+        pkv.paged_decode_attn_multi(out, q[:, None], fp8_pool, fp8_pool, bt, cl, 0.1, 64)
+    with pytest.raises(ValueError, match="2-byte elements"):
+        pkv.kv_append_fp8(bf16_pool, bf16_pool, q, q, None, None, cl.long())
+
+
 def test_binding_refuses_to_run_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(pkv, "_LIB", None)
     monkeypatch.setattr(pkv, "library_path", lambda: str(tmp_path / "missing.so"))
