@@ -154,8 +154,10 @@ struct RingTiles {
 };
 // Tiles per sequence and their exclusive prefix in LDS (which the ring aliases: the function
 // ends with a workgroup barrier after its last LDS read), this wave's chunk (XCD-weighted
-// when `may_weight` and the call is large), and the tables.  ROW = bytes per K or V row.
-template <int ROW, int WPG>
+// when `may_weight` and the call is large), and the tables.  ROW = bytes per K or V row;
+// MULTI: also the lengths and the first tile's index (RingTiles::len, tt_first), and lengths
+// from fixed_len when context_lens is null (the single-token kernel needs none of these).
+template <int ROW, int WPG, bool MULTI>
 __device__ __forceinline__ void ring_setup(const RingWalk& g, int bid, lds_u8_t* lds,
                                            bool may_weight, RingTiles& t) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -172,7 +174,7 @@ __device__ __forceinline__ void ring_setup(const RingWalk& g, int bid, lds_u8_t*
   for (int i = 0; i < per; ++i) {
     const int bi = tid * per + i;
     if (bi < B) {
-      int L = g.context_lens ? g.context_lens[bi] : g.fixed_len;
+      int L = (!MULTI || g.context_lens) ? g.context_lens[bi] : g.fixed_len;
       L = L < 0 ? 0 : (L > cap ? cap : L);
       s_len[bi] = L;
       local += (L + kTile - 1) / kTile;
@@ -242,17 +244,17 @@ __device__ __forceinline__ void ring_setup(const RingWalk& g, int bid, lds_u8_t*
     int hi_[kRingTilesPerLane];
 #pragma unroll
     for (int j = 0; j < kRingTilesPerLane; ++j) hi_[j] = B - 1;
+    // branch-free: with lo == hi, mid = lo and s_pre[lo] <= rem, so a step changes nothing
 #pragma unroll 1
     for (int step = 0; step < 13; ++step) {
       bool any = false;
 #pragma unroll
       for (int j = 0; j < kRingTilesPerLane; ++j) {
-        if (lo_[j] < hi_[j]) {
-          const int mid = (lo_[j] + hi_[j] + 1) >> 1;
-          if (s_pre[mid] <= rem_[j]) lo_[j] = mid;
-          else hi_[j] = mid - 1;
-          any = true;
-        }
+        const int mid = (lo_[j] + hi_[j] + 1) >> 1;
+        const bool go = s_pre[mid] <= rem_[j];
+        lo_[j] = go ? mid : lo_[j];
+        hi_[j] = go ? hi_[j] : mid - 1;
+        any |= lo_[j] < hi_[j];
       }
       if (!wave_any(any)) break;
     }
@@ -260,11 +262,11 @@ __device__ __forceinline__ void ring_setup(const RingWalk& g, int bid, lds_u8_t*
     for (int j = 0; j < kRingTilesPerLane; ++j) {
       t.off[j] = 0;
       t.info[j] = 0;
-      t.len[j] = 0;
+      if constexpr (MULTI) t.len[j] = 0;
       const int n = kWave * j + lane;
       if (n < ntl) {
         const int tt = rem_[j] - s_pre[lo_[j]];
-        if (j == 0) tt_l = tt;
+        if (MULTI && j == 0) tt_l = tt;
         const int L = s_len[lo_[j]];
         const int blk = tiles_per_block == 1 ? tt : tt / tiles_per_block;
         const int tin = tiles_per_block == 1 ? 0 : tt - blk * tiles_per_block;
@@ -275,11 +277,11 @@ __device__ __forceinline__ void ring_setup(const RingWalk& g, int bid, lds_u8_t*
                              (uint64_t)tin * (kTile * ROW);
         t.off[j] = (uint32_t)(off >> 8);
         t.info[j] = (ok ? min(kTile, L - tt * kTile) : 0) | ((gg_[j] * B + lo_[j]) << 5);
-        t.len[j] = L;
+        if constexpr (MULTI) t.len[j] = L;
       }
     }
   }
-  t.tt_first = __builtin_amdgcn_readlane(tt_l, 0);
+  if constexpr (MULTI) t.tt_first = __builtin_amdgcn_readlane(tt_l, 0);
   // the prefix area is reused by the ring from here on
   __syncthreads();
 
@@ -307,7 +309,7 @@ __device__ __forceinline__ void gqa_ring_body(const DecodeArgs& a, int bid, lds_
                     a.num_blocks, min(a.max_blocks * a.block_size, a.max_context_len), a.chunks,
                     a.ws_prefix, a.ws_seg};
   RingTiles tl;
-  ring_setup<Lo::ROW, WPG>(gw, bid, lds, WPG == 4, tl);
+  ring_setup<Lo::ROW, WPG, false>(gw, bid, lds, WPG == 4, tl);
   const int ntl = tl.ntl, ch = tl.ch;
   if (ntl <= 0) return;
   uint32_t (&off_l)[kRingTilesPerLane] = tl.off;
