@@ -65,6 +65,8 @@ constexpr int kMaxMlaSeqs = 4096;
 constexpr int kMaxChunkStages = 128;                // two per lane
 constexpr int kPRow = 80;                           // bytes per head row of P (32 fp16 + pad)
 constexpr float kSlack = 8.0f;
+constexpr int kScoreGroup = 3;                      // score products per group of K reads
+constexpr int kPieceStartStages = 5;                // measured cost of a piece start, in stages
 static_assert(kStageBytes % (16 * kWave * kDmaWaves) == 0, "stage split");
 
 __device__ __forceinline__ f32x4_t mfma_bf16(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
@@ -522,7 +524,17 @@ __global__ __launch_bounds__(8 * kWave, 1) void mla_split_kernel(MlaArgs a) {
   auto nstages = [&](int bi) { return (clamp_len(a.context_lens[bi]) + kStage - 1) / kStage; };
   const bool wave_scan = B <= kWave;
   int pre_l = 0, len_l = 0;  // register scan: sequence `lane`'s first stage and length
-  int T;
+  int T, PV;
+  // Virtual stages placed before every sequence, so that a chunk in which a piece starts
+  // (q loaded, the closed piece's partials stored) gets correspondingly fewer stages.  Only
+  // with at least one stage per chunk (the merge takes every chunk of a segment's range as
+  // written) and while every chunk stays within kMaxChunkStages.
+  auto piece_pad = [&](int T_) {
+    return T_ >= C && (long long)T_ + (long long)kPieceStartStages * B <=
+                          (long long)(kMaxChunkStages - 1) * C
+               ? kPieceStartStages
+               : 0;
+  };
   if (wave_scan) {
     len_l = lane < B ? clamp_len(a.context_lens[lane]) : 0;
     const int ns_l = (len_l + kStage - 1) / kStage;
@@ -534,10 +546,12 @@ __global__ __launch_bounds__(8 * kWave, 1) void mla_split_kernel(MlaArgs a) {
     }
     pre_l = incl - ns_l;
     T = __builtin_amdgcn_readlane(incl, kWave - 1);
+    PV = piece_pad(T);
     if (blockIdx.x == 0 && w == 0) {
       if (lane < B) {
         a.ws_prefix[lane] = pre_l;
-        segment_range(pre_l, ns_l, T, C, a.ws_seg + 2 * lane);
+        segment_range(pre_l + (long long)PV * (lane + 1), ns_l, (long long)T + (long long)PV * B, C,
+                      a.ws_seg + 2 * lane);
       }
       if (lane == 0) a.ws_prefix[B] = T;
     }
@@ -564,17 +578,43 @@ __global__ __launch_bounds__(8 * kWave, 1) void mla_split_kernel(MlaArgs a) {
     }
     if (tid == 0) s_pre[B] = s_sum[THREADS - 1];
     __syncthreads();
+    T = __builtin_amdgcn_readfirstlane(s_pre[B]);
+    PV = piece_pad(T);
     if (blockIdx.x == 0) {
       for (int i = tid; i <= B; i += THREADS) a.ws_prefix[i] = s_pre[i];
-      write_segment_ranges(a.ws_seg, s_pre, B, 1, C, tid, THREADS);
+      for (int b = tid; b < B; b += THREADS)
+        segment_range(s_pre[b] + (long long)PV * (b + 1), s_pre[b + 1] - s_pre[b],
+                      (long long)T + (long long)PV * B, C, a.ws_seg + 2 * b);
     }
-    T = __builtin_amdgcn_readfirstlane(s_pre[B]);
   }
 
-  // ---- this workgroup's head group and chunk (head groups of a chunk on one XCD)
+  // ---- this workgroup's head group and chunk (head groups of a chunk on one XCD).  The
+  // chunks are equal ranges of the stage space with PV virtual stages before each sequence
+  // (sequence b's stages sit at virtual positions pre[b] + PV (b + 1) ..); a chunk takes the
+  // real stages inside its range, which are contiguous.
   const int x = blockIdx.x, xcd = x & 7, kx = x >> 3;
   const int hg = kx % HG, ch = (kx / HG) * 8 + xcd;
-  const long long tb = (long long)T * ch / C, te = (long long)T * (ch + 1) / C;
+  const long long Tv = (long long)T + (long long)PV * B;
+  auto real_before = [&](long long v) -> long long {  // real stages before virtual position v
+    if (PV == 0) return v;
+    int pads;
+    if (wave_scan) {  // all lanes take part: sum over sequences of their pads before v
+      const long long vp = (long long)pre_l + (long long)PV * lane;
+      pads = lane < B ? (int)min(max(v - vp, 0LL), (long long)PV) : 0;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) pads += __shfl_xor(pads, off);
+    } else {  // the last sequence whose pads start at or before v (sequence 0's start at 0)
+      int lo = 0, hi = B - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((long long)s_pre[mid] + (long long)PV * mid <= v) lo = mid;
+        else hi = mid - 1;
+      }
+      pads = PV * lo + (int)min(v - ((long long)s_pre[lo] + (long long)PV * lo), (long long)PV);
+    }
+    return v - __builtin_amdgcn_readfirstlane(pads);  // the same in every lane
+  };
+  const long long tb = real_before(Tv * ch / C), te = real_before(Tv * (ch + 1) / C);
   const int ns = (int)min(te - tb, (long long)kMaxChunkStages);
 
   // ---- per-stage first token (pool row index) and valid-token count | sequence << 6,
@@ -737,23 +777,34 @@ __global__ __launch_bounds__(8 * kWave, 1) void mla_split_kernel(MlaArgs a) {
         l_part = 0.f;
       }
       const uint8_t* buf = sbuf + (n % NBUF) * kStageBytes;
-      // S^T = K Q^T for both token tiles (two independent accumulation chains)
+      // S^T = K Q^T for both token tiles (two independent accumulation chains).  The K
+      // fragments are read in groups of KG products, each group's reads issued before the
+      // previous group's products (two groups in registers, at most 4 KG reads in flight:
+      // within the LDS counter's range), so that no product waits on a read issued just
+      // before it.
       f32x4_t s[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+      constexpr int KG = kScoreGroup, NGRP = kDqk / 32 / KG;
+      bf16x8_t kf[2][2][KG];  // [group parity][token tile][product]
+      auto read_group = [&](int grp, bf16x8_t (&dst)[2][KG]) {
 #pragma unroll
-      for (int k0 = 0; k0 < kDqk / 32; k0 += 6) {
-        bf16x8_t kf[2][6];
-#pragma unroll
-        for (int ks = 0; ks < 6; ++ks)
+        for (int ks = 0; ks < KG; ++ks)
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
-            const int kk = k0 + ks;
+            const int kk = grp * KG + ks;
             const int off = kk < 16 ? k_main[tt][kk & 7] + 128 * (kk >> 3) : k_tail[tt][kk - 16];
-            kf[tt][ks] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(buf + off));
+            dst[tt][ks] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(buf + off));
           }
+      };
+      read_group(0, kf[0]);
 #pragma unroll
-        for (int ks = 0; ks < 6; ++ks)
+      for (int grp = 0; grp < NGRP; ++grp) {
+        if (grp + 1 < NGRP) read_group(grp + 1, kf[(grp + 1) & 1]);
+        sched_fence();
 #pragma unroll
-          for (int tt = 0; tt < 2; ++tt) s[tt] = mfma_bf16(kf[tt][ks], qf[k0 + ks], s[tt]);
+        for (int ks = 0; ks < KG; ++ks)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) s[tt] = mfma_bf16(kf[grp & 1][tt][ks], qf[grp * KG + ks], s[tt]);
+        sched_fence();
       }
 
       // online softmax (log2 domain): lane holds tokens tt * 16 + 4 g + r of head i16.  The

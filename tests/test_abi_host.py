@@ -5,6 +5,8 @@ import ctypes
 import os
 import re
 
+import numpy as np
+
 import pytest
 
 import paged_kv_cache_288_amd as pkv
@@ -296,6 +298,83 @@ def test_mla_balanced_workspace_size(lib):
     # Hq not a multiple of 32 (and explicit partitions) use the partitioned kernel
     assert lib.pkv_mla_workspace_bytes(2, 48, 512, 8192, 0) > 0
     assert lib.pkv_mla_workspace_bytes(2, 128, 512, 512, 1024) == 0
+
+
+def _mla_padded_split(ns_b, C, pad, max_stages=128):
+    """Mirror of the latent kernel's chunking: `pad` virtual stages before every sequence
+    (when the total allows), chunk c takes the real stages inside [Tv c / C, Tv (c+1) / C);
+    returns the pad used, each chunk's real [tb, te) and each sequence's (first chunk, count)
+    as the kernel writes them for the merge."""
+    B, T = len(ns_b), int(sum(ns_b))
+    pre = [0]
+    for n in ns_b:
+        pre.append(pre[-1] + int(n))
+    pv = pad if (T >= C and T + pad * B <= (max_stages - 1) * C) else 0
+    tv = T + pv * B
+
+    def real_before_sum(v):            # the register-scan form (sequences up to 64)
+        return v - sum(min(max(v - (pre[b] + pv * b), 0), pv) for b in range(B))
+
+    def real_before_search(v):         # the binary-search form (more sequences)
+        if pv == 0:
+            return v
+        lo, hi = 0, B - 1
+        while lo < hi:
+            mid = (lo + hi + 1) >> 1
+            if pre[mid] + pv * mid <= v:
+                lo = mid
+            else:
+                hi = mid - 1
+        return v - (pv * lo + min(v - (pre[lo] + pv * lo), pv))
+
+    chunks = []
+    for c in range(C):
+        a, b = tv * c // C, tv * (c + 1) // C
+        tb, te = real_before_sum(a), real_before_sum(b)
+        assert (tb, te) == (real_before_search(a), real_before_search(b))
+        chunks.append((tb, te))
+    chunk_of = lambda t: ((t + 1) * C - 1) // tv
+    segs = []
+    for b in range(B):
+        if ns_b[b] == 0:
+            segs.append((0, 0))
+            continue
+        first = pre[b] + pv * (b + 1)
+        c0 = chunk_of(first)
+        segs.append((c0, chunk_of(first + ns_b[b] - 1) - c0 + 1))
+    return pv, pre, chunks, segs
+
+
+def test_latent_chunks_with_piece_padding():
+    """Latent chunking with virtual stages before each sequence: the chunks' real ranges
+    tile the stages in order, every chunk in a sequence's merge range holds stages of it
+    (and no other chunk does), and no chunk exceeds 128 stages."""
+    rng = np.random.default_rng(5)
+    cases = [([64, 116, 236, 220, 108, 175] * 5 + [100, 90], 128, 4),   # latent batch-like
+             ([10] * 200, 128, 4), ([0, 0, 50, 0, 300], 16, 4), ([1] * 300, 8, 4),
+             ([128 * 8 - 10], 8, 4), ([5, 5], 64, 4)]
+    for _ in range(60):
+        B = int(rng.integers(1, 90))
+        ns_b = [int(x) for x in rng.integers(0, 260, size=B)]
+        C = int(rng.choice([8, 16, 64, 128, 256]))
+        cases.append((ns_b, C, int(rng.integers(1, 6))))
+    for ns_b, C, pad in cases:
+        T = sum(ns_b)
+        if T > 127 * C:
+            continue
+        pv, pre, chunks, segs = _mla_padded_split(ns_b, C, pad)
+        assert chunks[0][0] == 0 and chunks[-1][1] == T
+        for c in range(C - 1):
+            assert chunks[c][1] == chunks[c + 1][0]
+        if pv:
+            assert T >= C and max(te - tb for tb, te in chunks) <= 128
+        for b, (c0, n) in enumerate(segs):
+            lo, hi = pre[b], pre[b + 1]
+            holding = [c for c, (tb, te) in enumerate(chunks) if max(tb, lo) < min(te, hi)]
+            if T >= C:
+                assert holding == list(range(c0, c0 + n)), (ns_b, C, pad, b)
+            else:  # fewer stages than chunks (never padded): the merge skips empty chunks
+                assert pv == 0 and set(holding) <= set(range(c0, c0 + n))
 
 
 def test_graph_calls_reject_null_arguments(lib):
