@@ -32,6 +32,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void gqa_stream_kernel(DecodeArg
 // One wave per (sequence, query head), kMergeWaves of them per workgroup.
 constexpr int kMergeWaves = 4;
 constexpr int kFastPieces = 16;  // pieces per segment merged in a single round trip
+constexpr int kFastLatentPieces = 8;  // the same for the latent (512-dim) rows
 template <int D>
 __global__ __launch_bounds__(kMergeWaves * kWave) void stream_merge_kernel(DecodeArgs a) {
   constexpr int PER = D / kWave;
@@ -58,6 +59,56 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void stream_merge_kernel(Decod
     const long long cc = c0 + i;
     return T * cc / a.chunks != T * (cc + 1) / a.chunks;
   };
+  if constexpr (D == 512) {
+    // Latent rows (2 KiB) of up to kFastLatentPieces pieces: every piece's m, l and row
+    // requested at once, as below; rows of pieces without weight are loaded but not used.
+    constexpr int NP = kFastLatentPieces, V4 = D / 4 / kWave;
+    if (np <= NP) {
+      float mp = kNegInf, lp = 0.f;
+      if (lane < np && live(lane)) {
+        mp = a.ws_m[(slot0 + lane) * G + h];
+        lp = a.ws_l[(slot0 + lane) * G + h];
+      }
+      float4 x[NP][V4];
+#pragma unroll
+      for (int u = 0; u < NP; ++u) {
+        const float* row = a.ws_o + ((slot0 + (u < np ? u : 0)) * G + h) * D;
+#pragma unroll
+        for (int i = 0; i < V4; ++i)
+          x[u][i] = u < np ? *(const float4*)(row + 4 * (lane + kWave * i))
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      float M = mp;
+#pragma unroll
+      for (int s = 32; s >= 1; s >>= 1) M = fmaxf(M, __shfl_xor(M, s));
+      const float f = (mp == kNegInf) ? 0.f : fast_exp2(mp - M);
+      float den = f * lp;
+#pragma unroll
+      for (int s = 32; s >= 1; s >>= 1) den += __shfl_xor(den, s);
+      float4 acc[V4];
+#pragma unroll
+      for (int i = 0; i < V4; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < NP; ++u) {
+        const float fu = __shfl(f, u);
+        if (fu != 0.f) {
+#pragma unroll
+          for (int i = 0; i < V4; ++i) {
+            acc[i].x += fu * x[u][i].x;
+            acc[i].y += fu * x[u][i].y;
+            acc[i].z += fu * x[u][i].z;
+            acc[i].w += fu * x[u][i].w;
+          }
+        }
+      }
+      const float sc = den > 0.f ? 1.f / den : 0.f;
+#pragma unroll
+      for (int i = 0; i < V4; ++i)
+        *(float4*)(out + 4 * (lane + kWave * i)) =
+            make_float4(acc[i].x * sc, acc[i].y * sc, acc[i].z * sc, acc[i].w * sc);
+      return;
+    }
+  }
   if constexpr (D <= 128) {
     // Up to kFastPieces pieces: every piece's m, l and o row requested at once (one round
     // trip), the weights formed afterwards; rows of pieces that carry no weight (empty

@@ -65,7 +65,8 @@ constexpr int kMaxMlaSeqs = 4096;
 constexpr int kMaxChunkStages = 128;                // two per lane
 constexpr int kPRow = 80;                           // bytes per head row of P (32 fp16 + pad)
 constexpr float kSlack = 8.0f;
-constexpr int kScoreGroup = 3;                      // score products per group of K reads
+constexpr int kScoreGroup = 2;                      // score products per group of K reads
+constexpr int kPvWaves = 8;                         // p.V waves of mla_split_kernel
 constexpr int kPieceStartStages = 5;                // measured cost of a piece start, in stages
 static_assert(kStageBytes % (16 * kWave * kDmaWaves) == 0, "stage split");
 
@@ -491,11 +492,12 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_stream_kernel(MlaArgs a) {
 // there is one workgroup barrier per stage.  P and the rescale factors are double-buffered by
 // stage parity; the copy of stage n + NBUF - 2 reuses the buffer of stage n - 2, which both
 // kinds of wave are done with by the barrier of iteration n.
-template <int NBUF>
-__global__ __launch_bounds__(8 * kWave, 1) void mla_split_kernel(MlaArgs a) {
-  constexpr int THREADS = 8 * kWave;
+template <int NBUF, int PVW>
+__global__ __launch_bounds__((4 + PVW) * kWave, 1) void mla_split_kernel(MlaArgs a) {
+  constexpr int THREADS = (4 + PVW) * kWave;
   constexpr int HT = 4, HPU = 64;  // head tiles and heads per workgroup
-  constexpr int DPW = 128, NT = 8; // accumulator: output dims, p.V products per head tile
+  constexpr int DPW = kDv / PVW, NT = DPW / 16;  // accumulator: output dims, p.V products per head tile
+  static_assert(PVW == 4 || PVW == 8, "p.V waves");
   static_assert(NBUF >= 4, "two stages in flight");
   __shared__ __attribute__((aligned(16))) uint8_t sbuf[NBUF * kStageBytes];
   // P of a stage in four 1 KiB slabs: slab k holds k-operand positions 8 k .. 8 k + 7 of
@@ -509,7 +511,9 @@ __global__ __launch_bounds__(8 * kWave, 1) void mla_split_kernel(MlaArgs a) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
   const bool scorer = w < 4;
-  const int r4 = w & 3;  // head tile (scorer) or output-dim slice (accumulator)
+  const int r4 = w & 3;                // head tile of a score wave
+  const int pvj = scorer ? 0 : w - 4;  // output-dim slice of a p.V wave
+  const bool copier = !scorer && pvj < 4;  // the first four p.V waves copy the stages
   const int i16 = lane & 15, g = lane >> 4;
   const int B = a.B, Hq = a.Hq, HG = Hq / HPU, C = a.chunks;
   const int cap = min(a.max_blocks * kBlock, a.max_context_len);
@@ -690,33 +694,33 @@ __global__ __launch_bounds__(8 * kWave, 1) void mla_split_kernel(MlaArgs a) {
   uint32_t dma_off[kDmaPerWave];
 #pragma unroll
   for (int j = 0; j < kDmaPerWave; ++j) {
-    const int c = (r4 * kDmaPerWave + j) * kWave + lane;
+    const int c = (pvj * kDmaPerWave + j) * kWave + lane;
     const int t = c / kRowChunks, pp = c % kRowChunks;
     dma_off[j] = (uint32_t)(16 * (t * kRowChunks + (pp ^ split_swizzle(t))));
   }
   const uint32_t sbuf_lds = (uint32_t)(uintptr_t)(lds_void_t*)sbuf;
   auto issue_stage = [&](int n) {
-    if (scorer) return;
+    if (!copier) return;
     const i32x4_t src = stage_src(n);
-    const uint32_t base = sbuf_lds + (n % NBUF) * kStageBytes + r4 * kDmaPerWave * 1024;
+    const uint32_t base = sbuf_lds + (n % NBUF) * kStageBytes + pvj * kDmaPerWave * 1024;
 #pragma unroll
     for (int j = 0; j < kDmaPerWave; ++j) lds_copy16(src, dma_off[j], base + j * 1024);
   };
 
   // ---- scorer: K (A operand) of token tile tt.  Product ks < 16 contracts chunk ks + 16 g
   // (lane group g), products 16 and 17 the tail chunks 64 + 4 (ks - 16) + split_tail(g);
-  // q is loaded with the same chunk assignment.  k_main[tt][e] is the offset of chunk
-  // 16 g + e (e < 8; chunks 16 g + 8 + e are 128 bytes further), k_tail[tt][ks - 16] of the
-  // tail chunk.
+  // q is loaded with the same chunk assignment.  k_main[e] is the offset of chunk 16 g + e of
+  // row i16 (e < 8; chunks 16 g + 8 + e are 128 bytes further), k_tail[ks - 16] of the tail
+  // chunk; row i16 + 16 (token tile 1) has the same swizzle, kTileRows bytes further.
   const int tail_g = 2 * (g & 1) + (g >> 1);
-  int k_main[2][8], k_tail[2][2];
+  constexpr int kTileRows = 16 * kRow;
+  int k_main[8], k_tail[2];
+  {
+    const int t = i16, sw = split_swizzle(t);
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int t = tt * 16 + i16, sw = split_swizzle(t);
+    for (int e = 0; e < 8; ++e) k_main[e] = 16 * (t * kRowChunks + 16 * g + (e ^ sw));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) k_main[tt][e] = 16 * (t * kRowChunks + 16 * g + (e ^ sw));
-#pragma unroll
-    for (int k = 0; k < 2; ++k) k_tail[tt][k] = 16 * (t * kRowChunks + 64 + ((4 * k + tail_g) ^ sw));
+    for (int k = 0; k < 2; ++k) k_tail[k] = 16 * (t * kRowChunks + 64 + ((4 * k + tail_g) ^ sw));
   }
   // ---- accumulator: V (B operand, transposed reads) for dims 128 r4 + 16 nt + i16.  Read h
   // of lane group g takes the 4-token block 4 (g >> 1) + 2 h + (g & 1) (so that each 32-lane
@@ -728,7 +732,7 @@ __global__ __launch_bounds__(8 * kWave, 1) void mla_split_kernel(MlaArgs a) {
     const int qd = (i16 & 3) >> 1, half8 = 8 * (i16 & 1);
 #pragma unroll
     for (int n4 = 0; n4 < 4; ++n4)
-      v_off[h][n4] = 16 * (t * kRowChunks + 16 * r4 + ((2 * n4 + qd) ^ split_swizzle(t))) + half8;
+      v_off[h][n4] = 16 * (t * kRowChunks + (DPW / 8) * pvj + ((2 * n4 + qd) ^ split_swizzle(t))) + half8;
   }
 
   const float cscale = a.scale * kLog2e;
@@ -791,7 +795,8 @@ __global__ __launch_bounds__(8 * kWave, 1) void mla_split_kernel(MlaArgs a) {
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
             const int kk = grp * KG + ks;
-            const int off = kk < 16 ? k_main[tt][kk & 7] + 128 * (kk >> 3) : k_tail[tt][kk - 16];
+            const int off =
+                tt * kTileRows + (kk < 16 ? k_main[kk & 7] + 128 * (kk >> 3) : k_tail[kk - 16]);
             dst[tt][ks] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(buf + off));
           }
       };
@@ -853,7 +858,8 @@ __global__ __launch_bounds__(8 * kWave, 1) void mla_split_kernel(MlaArgs a) {
       for (int nt = 0; nt < NT; ++nt) o[ht][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};  // finite for alpha = 0
     for (int n = 0; n < NBUF - 2; ++n) issue_stage(n);
     for (int n = 0; n <= ns; ++n) {
-      barrier_vm<kDmaPerWave * (NBUF - 3)>();
+      if (copier) barrier_vm<kDmaPerWave * (NBUF - 3)>();  // this wave's copies of stage n
+      else barrier_vm<63>();
       issue_stage(n + NBUF - 2);
       if (n == 0) continue;
       const int pn = n - 1;
@@ -911,7 +917,7 @@ __global__ __launch_bounds__(8 * kWave, 1) void mla_split_kernel(MlaArgs a) {
           for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              a.ws_o[(row0 + ht * 16 + 4 * g + r) * kDv + DPW * r4 + 16 * nt + i16] = o[ht][nt][r];
+              a.ws_o[(row0 + ht * 16 + 4 * g + r) * kDv + DPW * pvj + 16 * nt + i16] = o[ht][nt][r];
       }
     }
   }
@@ -935,7 +941,7 @@ hipError_t launch_mla_stream(const MlaArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)(a.Hq / hpu * a.chunks));
   if (hpu == 64)
-    hipLaunchKernelGGL((mla_split_kernel<NBUF>), grid, dim3(8 * kWave), 0, s, a);
+    hipLaunchKernelGGL((mla_split_kernel<NBUF, kPvWaves>), grid, dim3((4 + kPvWaves) * kWave), 0, s, a);
   else
     hipLaunchKernelGGL((mla_stream_kernel<2, NBUF>), grid, dim3(kMThreads), 0, s, a);
   hipError_t e = hipGetLastError();
