@@ -485,13 +485,14 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_stream_kernel(MlaArgs a) {
   wait_vm<0>();
 }
 
-// Role-split variant for 64-head groups, 8 waves: waves 0-3 ("scorers") take stage n - scores
-// for one 16-head tile over all 32 tokens, the online softmax, P into LDS - while waves 4-7
-// ("accumulators") run p.V of stage n - 1 for 128 output dims each and copy the stages
-// HBM -> LDS.  Each SIMD holds one wave of each kind, so score and p.V products overlap, and
-// there is one workgroup barrier per stage.  P and the rescale factors are double-buffered by
-// stage parity; the copy of stage n + NBUF - 2 reuses the buffer of stage n - 2, which both
-// kinds of wave are done with by the barrier of iteration n.
+// Role-split variant for 64-head groups, 4 + PVW waves: waves 0-3 ("scorers") take stage n -
+// scores for one 16-head tile over all 32 tokens, the online softmax, P into LDS - while the
+// PVW waves after them ("accumulators") run p.V of stage n - 1 for 512 / PVW output dims
+// each, the first four also copying the stages HBM -> LDS.  Each SIMD holds one score wave
+// and PVW / 4 p.V waves, so score and p.V products overlap, and there is one workgroup
+// barrier per stage.  P and the rescale factors are double-buffered by stage parity; the copy
+// of stage n + NBUF - 2 reuses the buffer of stage n - 2, which every wave is done with by
+// the barrier of iteration n.
 template <int NBUF, int PVW>
 __global__ __launch_bounds__((4 + PVW) * kWave, 1) void mla_split_kernel(MlaArgs a) {
   constexpr int THREADS = (4 + PVW) * kWave;
