@@ -49,6 +49,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void cascade_kernel(DecodeArgs t
 // single-token balanced kernel) and the prefix pieces of segment (g, b / J), row
 // (b % J) * G + h % G (rows of J * G, from the multi-token kernel).  One wave per output row.
 constexpr int kCascadeMergeWaves = 4;
+constexpr int kCascadeFastPieces = 8;  // per set, merged in one round trip
 template <int D>
 __global__ __launch_bounds__(kCascadeMergeWaves * kWave) void cascade_merge_kernel(CascadeMergeArgs a) {
   constexpr int PER = D / kWave;
@@ -87,6 +88,60 @@ __global__ __launch_bounds__(kCascadeMergeWaves * kWave) void cascade_merge_kern
     const long long cc = st.c0 + i;
     return st.T * cc / st.chunks != st.T * (cc + 1) / st.chunks;
   };
+  // Up to kCascadeFastPieces pieces in each set: every piece's m, l and row requested at
+  // once (one round trip instead of one per set and step); rows of pieces without weight
+  // (empty chunks: never written) are loaded but not used.
+  if (sets[0].np <= kCascadeFastPieces && sets[1].np <= kCascadeFastPieces) {
+    constexpr int NP = 2 * kCascadeFastPieces, LPR = D / 4, RPW = kWave / LPR, U = NP / RPW;
+    const int sub = lane / LPR, col = lane % LPR;
+    // lane j < NP: piece j of set j / kCascadeFastPieces
+    const int ks = lane / kCascadeFastPieces, kp = lane % kCascadeFastPieces;
+    float mp = kNegInf, lp = 0.f;
+    const Set& sl = (ks & 1) ? sets[1] : sets[0];
+    if (lane < NP && kp < sl.np && live(sl, kp)) {
+      const Set& st = sl;
+      const size_t si = (st.slot0 + kp) * st.rows + st.row;
+      mp = st.m[si];
+      lp = st.l[si];
+    }
+    float4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = u * RPW + sub, k = j / kCascadeFastPieces, p = j % kCascadeFastPieces;
+      const Set& st = sets[k];
+      x[u] = p < st.np ? *(const float4*)(st.o + ((st.slot0 + p) * st.rows + st.row) * D + 4 * col)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float M = mp;
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) M = fmaxf(M, __shfl_xor(M, s));
+    const float f = (mp == kNegInf) ? 0.f : fast_exp2(mp - M);
+    float den = f * lp;
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) den += __shfl_xor(den, s);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float fj = __shfl(f, u * RPW + sub);
+      if (fj != 0.f) {
+        acc.x += fj * x[u].x;
+        acc.y += fj * x[u].y;
+        acc.z += fj * x[u].z;
+        acc.w += fj * x[u].w;
+      }
+    }
+#pragma unroll
+    for (int m = LPR; m < kWave; m <<= 1) {
+      acc.x += __shfl_xor(acc.x, m);
+      acc.y += __shfl_xor(acc.y, m);
+      acc.z += __shfl_xor(acc.z, m);
+      acc.w += __shfl_xor(acc.w, m);
+    }
+    const float sc = den > 0.f ? 1.f / den : 0.f;  // no token at all: zeros
+    if (lane < LPR)
+      *(float4*)(out + 4 * lane) = make_float4(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
+    return;
+  }
   float M = kNegInf;
 #pragma unroll
   for (int k = 0; k < 2; ++k)
