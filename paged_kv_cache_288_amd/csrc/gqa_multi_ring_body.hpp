@@ -56,7 +56,8 @@ __device__ __forceinline__ void gqa_multi_ring_body(const MultiArgs& a, int bid,
 
   const RingWalk gw{a.fixed_len >= 0 ? nullptr : a.context_lens, a.fixed_len, a.block_table,
                     (size_t)a.table_stride, B, a.Hkv, a.block_size, a.num_blocks,
-                    min(a.max_blocks * a.block_size, a.max_len), a.chunks, a.ws_prefix, a.ws_seg};
+                    min(a.max_blocks * a.block_size, a.max_len), a.chunks, a.ws_prefix, a.ws_seg,
+                    a.xcd8};
   RingTiles tl;
   ring_setup<M::ROW, WPG, true>(gw, bid, lds, true, tl);  // XCD-weighted ranges for large calls
   const int ntl = tl.ntl, ch = tl.ch;

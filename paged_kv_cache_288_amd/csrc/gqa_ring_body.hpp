@@ -52,6 +52,13 @@ __device__ __forceinline__ uint2 lds_ld8(const lds_u8_t* base, uint32_t off) {
   return uint2{v[0], v[1]};
 }
 
+// Index (0..7) of the XCD running this wave, from the XCC_ID hardware register.
+__device__ __forceinline__ int xcd_id() {
+  uint32_t x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+  return (int)(x & 7u);
+}
+
 // Raw buffer resource words over [base, base + bytes), for loads issued from assembly.
 __device__ __forceinline__ i32x4_t ring_rsrc(const void* base, uint32_t bytes) {
   const uint64_t p = (uint64_t)base;
@@ -139,6 +146,7 @@ struct RingWalk {
   int chunks;
   int32_t* ws_prefix;           // written by workgroup 0: tile prefix [B + 1]
   int32_t* ws_seg;              //   and per segment its first chunk and chunk count
+  int xcd8;                     // the grid is spread over 8 XCDs in turn (weighting by XCD id)
 };
 // One wave's chunk: per lane, kRingTilesPerLane tiles (tile n of the chunk in entry n / 64 of
 // lane n % 64): byte offset / 256 of its first row in the pools, valid tokens | segment << 5,
@@ -211,7 +219,15 @@ __device__ __forceinline__ void ring_setup(const RingWalk& g, int bid, lds_u8_t*
   }
 
   // ---- this wave's chunk and, per lane, kRingTilesPerLane tiles' offset, length, segment
-  const int ch = (bid & 7) * (C / 8) + (bid >> 3) * WPG + w;
+  // The workgroup's eighth of the chunks is bid mod 8.  Workgroups go to the 8 XCDs in turn,
+  // but which XCD takes workgroup 0 depends on the dispatches before this one, so weighted
+  // ranges (the heavier eighths meant for even XCDs) take the parity from the XCD that runs
+  // the workgroup: eighth (bid mod 8) xor f, f = (XCD id xor bid) & 1.  Workgroups 2j and
+  // 2j + 1 run on neighbouring XCDs, so both find the same f and still share the two eighths
+  // 2j mod 8 and 2j mod 8 + 1 between them.
+  int eighth = bid & 7;
+  if (wtd && g.xcd8) eighth ^= (xcd_id() ^ bid) & 1;
+  const int ch = eighth * (C / 8) + (bid >> 3) * WPG + w;
   const long long tb = xcd_chunk_start(ch, T, C, wtd), te = xcd_chunk_start(ch + 1, T, C, wtd);
   const int ntl = (int)min(te - tb, (long long)kRingMaxChunkTiles);
   t.ntl = ntl;
@@ -307,7 +323,7 @@ __device__ __forceinline__ void gqa_ring_body(const DecodeArgs& a, int bid, lds_
   const int B = a.B;
   const RingWalk gw{a.context_lens, 0, a.block_table, (size_t)a.max_blocks, B, a.Hkv, a.block_size,
                     a.num_blocks, min(a.max_blocks * a.block_size, a.max_context_len), a.chunks,
-                    a.ws_prefix, a.ws_seg};
+                    a.ws_prefix, a.ws_seg, a.xcd8};
   RingTiles tl;
   ring_setup<Lo::ROW, WPG, false>(gw, bid, lds, WPG == 4, tl);
   const int ntl = tl.ntl, ch = tl.ch;

@@ -115,6 +115,20 @@ int device_cus() {
   return cached[dev];
 }
 
+// Whether the current device hands a grid's workgroups to 8 XCDs in turn: the whole MI355X
+// as one partition (cached per device; false when the query fails).
+bool device_xcd8() {
+  static int cached[64] = {0};  // 0 unknown, 1 no, 2 yes
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  if (!cached[dev]) {
+    int n = 0;
+    const bool ok = hipDeviceGetAttribute(&n, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess;
+    cached[dev] = ok && n == 8 ? 2 : 1;
+  }
+  return cached[dev] == 2;
+}
+
 // Balanced mode: one chunk per resident wave (two 4-wave workgroups per CU for the
 // single-token kernel), and enough chunks that
 // none holds more than kMaxChunkTiles tiles even if every context were max_context_len;
@@ -361,7 +375,7 @@ pkv_status pkv_paged_decode_attn(float* out, const void* q, const void* k_pool,
     pkv::DecodeArgs a{out, (const uint16_t*)q, (const uint8_t*)k_pool, (const uint8_t*)v_pool,
                       k_scale, v_scale, block_table, context_lens, ws_m, ws_l, ws_o,
                       B, Hq, Hkv, d, block_size, num_blocks, max_blocks_per_seq, ctx,
-                      0, 0, scale, fp8 ? 1 : 0, chunks, ws_p, ws_s};
+                      0, 0, scale, fp8 ? 1 : 0, chunks, ws_p, ws_s, device_xcd8() ? 1 : 0};
     return hip_status(pkv::launch_gqa_stream(a, s));
   }
   const int32_t P = num_parts(ctx, ps);
@@ -537,6 +551,7 @@ pkv_status pkv_paged_decode_attn_multi(float* out, const void* q, const void* k_
   a.table_stride = max_blocks_per_seq, a.fixed_len = -1, a.q_rows = B * q_len;
   a.max_len = max_context_len;
   a.causal = 1, a.fp8 = fp8 ? 1 : 0, a.scale = scale, a.chunks = chunks;
+  a.xcd8 = device_xcd8() ? 1 : 0;
   return hip_status(pkv::launch_gqa_multi(a, (hipStream_t)stream));
 }
 
@@ -593,7 +608,7 @@ pkv_status pkv_paged_decode_attn_cascade(float* out, const void* q, const void* 
   pkv::DecodeArgs ta{out, (const uint16_t*)q, (const uint8_t*)k_pool, (const uint8_t*)v_pool,
                      k_scale, v_scale, tail_table, tail_lens, t_m, t_l, t_o,
                      B, Hq, Hkv, d, block_size, num_blocks, max_tail_blocks, max_tail_len,
-                     0, 0, scale, fp8 ? 1 : 0, c.t_chunks, t_p, t_s};
+                     0, 0, scale, fp8 ? 1 : 0, c.t_chunks, t_p, t_s, device_xcd8() ? 1 : 0};
   // prefix: groups of J sequences as the q_len rows of the multi-token kernel, all reading
   // the prefix blocks, no causal mask; launched together with the tails
   pkv::MultiArgs pa{};
@@ -615,6 +630,7 @@ pkv_status pkv_paged_decode_attn_cascade(float* out, const void* q, const void* 
     pa.max_blocks = prefix_len / block_size, pa.table_stride = 0, pa.fixed_len = prefix_len;
     pa.max_len = prefix_len;
     pa.q_rows = B, pa.causal = 0, pa.fp8 = fp8 ? 1 : 0, pa.scale = scale, pa.chunks = c.p_chunks;
+    pa.xcd8 = device_xcd8() ? 1 : 0;
     st = hip_status(pkv::launch_cascade(ta, pa, s));
   }
   if (st != PKV_OK) return st;

@@ -174,8 +174,10 @@ __device__ __forceinline__ void write_segment_ranges(int32_t* ws_seg, PRE pre, i
 
 // ---- XCD-weighted ranges.  On MI355X the odd-numbered XCDs were measured to stream the
 // single-token decode 6-10 % slower than the even ones on most boxes (their waves finished
-// 15-20 us later on a 200 us call), and workgroup i runs on XCD i mod 8.  The balanced
-// kernels give wave w of workgroup i the chunk (i mod 8) * C/8 + (i / 8) * waves + w, so
+// 15-20 us later on a 200 us call).  Workgroups go to the XCDs in turn: workgroup i runs on
+// XCD (i + r) mod 8, r the same for the whole grid but set by the dispatches before it.  The
+// balanced kernels give wave w of workgroup i the chunk e * C/8 + (i / 8) * waves + w, with
+// e = i mod 8 (weighted: with its lowest bit matched to the parity of the XCD it runs on), so
 // each XCD owns C/8 consecutive chunks.  (The multi-token kernel, at 8 waves per CU and
 // about 74 tiles per chunk on the 70B-shaped verify batch, measured 2.6 % slower
 // weighted, and splits evenly.)  Weighted, the chunks of even XCDs take 17

@@ -63,6 +63,9 @@ struct DecodeArgs {
   int32_t chunks;
   int32_t* ws_prefix;
   int32_t* ws_seg;
+  // 1 when the device hands a grid's workgroups to 8 XCDs in turn (the whole chip as one
+  // partition): the balanced kernels then read which XCD runs them to place weighted ranges
+  int32_t xcd8;
 };
 hipError_t launch_gqa_decode(const DecodeArgs& a, hipStream_t s);
 // Balanced mode: decode kernel + merge kernel (always both).
@@ -145,6 +148,7 @@ struct MultiArgs {
   int32_t causal, fp8;
   float scale;
   int32_t chunks;  // one per resident wave, a multiple of 32
+  int32_t xcd8;    // as DecodeArgs::xcd8
 };
 // Decode kernel + merge kernel.
 hipError_t launch_gqa_multi(const MultiArgs& a, hipStream_t s);

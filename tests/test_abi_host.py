@@ -225,6 +225,31 @@ def test_xcd_weighted_chunks(T, C):
         assert starts[c] <= t < starts[c + 1], (t, c)
 
 
+@pytest.mark.parametrize("groups", [1, 2, 4])
+def test_xcd_parity_assignment(groups):
+    """Host mirror of how a balanced kernel's workgroup picks its eighth of the chunks when
+    the ranges are weighted: eighth = (bid mod 8) xor f, f = (XCD id xor bid) & 1.  For every
+    XCD r that may take workgroup 0 (workgroup i then runs on XCD (i + r) mod 8), each chunk
+    goes to exactly one wave, and every eighth with the heavier (even) weight runs on an even
+    XCD.  With the parity taken from bid alone, an odd r puts every heavy eighth on an odd
+    XCD."""
+    WPG = 4
+    C = 8 * WPG * groups
+    for r in range(8):
+        owner = {}
+        for bid in range(C // WPG):
+            xcd = (bid + r) % 8
+            eighth = (bid % 8) ^ ((xcd ^ bid) & 1)
+            assert eighth % 2 == xcd % 2
+            for w in range(WPG):
+                ch = eighth * (C // 8) + (bid // 8) * WPG + w
+                assert ch not in owner
+                owner[ch] = xcd
+        assert sorted(owner) == list(range(C))
+        blind = [((bid + r) % 8) % 2 == (bid % 8) % 2 for bid in range(8)]
+        assert all(blind) == (r % 2 == 0)
+
+
 def test_mla_rejects_bad_arguments_before_launch(lib):
     f = lib.pkv_paged_decode_attn_mla
     base = [FAKE, FAKE, FAKE, FAKE, FAKE, 2, 128, 576, 512, 64, 10, 4, 200, 0.1, 0, None, 0, None]

@@ -103,6 +103,27 @@ def test_decode_full_size(name):
     assert_close(got, oracle_decode(w), w.kv_dtype, f"{name} full size, all {w.B} sequences")
 
 
+def test_weighted_ranges_do_not_depend_on_the_first_xcd():
+    """The 70B-shaped batch is large enough for XCD-weighted ranges, where a workgroup
+    reads which XCD runs it.  Which XCD takes workgroup 0 moves with the dispatches before a
+    call, so the decode is repeated after 1 to 7 extra one-workgroup launches of other work:
+    every output must equal the first bit for bit (the chunk ranges, and so every piece, do
+    not depend on where they run), and the first matches the oracle on sampled sequences."""
+    torch = torch_cuda()
+    w = make_workload("gqa70b")
+    dev = to_device(torch, w)
+    first = gpu_decode(torch, w, dev=dev)
+    x = torch.zeros(64, device="cuda")
+    for extra in range(1, 8):
+        for _ in range(extra):
+            x.add_(1.0)
+        got = gpu_decode(torch, w, dev=dev)
+        log(f"[decode] after {extra} extra launches: equal={np.array_equal(got, first)}")
+        assert np.array_equal(got.view(np.uint32), first.view(np.uint32)), extra
+    seqs = [0, 21, 63]
+    assert_close(first[seqs], oracle_decode(w, seqs), w.kv_dtype, "gqa70b sampled sequences")
+
+
 def test_splitk_partitioned_512_full_size():
     """The long-context batch through the partitioned kernel with 512-token partitions
     (64 per sequence and KV head), the split the workload names; all four sequences."""
