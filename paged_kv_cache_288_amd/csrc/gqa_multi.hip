@@ -62,8 +62,11 @@ __global__ __launch_bounds__(kMW * kWave, multi_waves_per_simd(D, RT)) void gqa_
 // One wave per (sequence, query token, KV head): the G rows are contiguous both in every
 // piece slot and in the output, so each piece is one G*D-float run read by the whole wave
 // (float4 per lane), and the output one run written by it.  Piece weights: lane q*G + h
-// holds piece p0 + q, row h, for 64/G pieces per pass.
+// holds piece p0 + q, row h, for 64/G pieces per pass.  Segments of up to kMultiFastPieces
+// pieces (the usual case: a few chunks per segment) are merged in one round trip: every
+// piece's m, l and run requested at once, the weights formed afterwards.
 constexpr int kMultiMergeWaves = 4;
+constexpr int kMultiFastPieces = 4;
 template <int D, int G>
 __global__ __launch_bounds__(kMultiMergeWaves * kWave) void multi_merge_kernel(MultiArgs a) {
   constexpr int RUN = G * D;                      // floats per piece run
@@ -107,6 +110,53 @@ __global__ __launch_bounds__(kMultiMergeWaves * kWave) void multi_merge_kernel(M
     for (int s = G; s < kWave; s <<= 1) x += __shfl_xor(x, s);
     return x;
   };
+  constexpr int NPF = kMultiFastPieces < PP ? kMultiFastPieces : PP;
+  if (np <= NPF) {
+    float mp = kNegInf, lp = 0.f;
+    if (qw < np && live(qw)) {
+      const size_t si = (slot0 + qw) * R + row0 + hw;
+      mp = a.ws_m[si];
+      lp = a.ws_l[si];
+    }
+    float4 x[NPF][NF4];
+#pragma unroll
+    for (int q = 0; q < NPF; ++q) {
+      const float* run = a.ws_o + ((slot0 + (q < np ? q : 0)) * R + row0) * D;
+#pragma unroll
+      for (int k = 0; k < NF4; ++k)
+        x[q][k] = (lane < ACTIVE && q < np) ? *(const float4*)(run + 4 * (lane + kWave * k))
+                                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const float M = row_max(mp);
+    const float f = (mp == kNegInf) ? 0.f : fast_exp2(mp - M);
+    const float den = row_sum(f * lp);
+    float4 acc[NF4];
+    float sc[NF4];
+#pragma unroll
+    for (int k = 0; k < NF4; ++k) {
+      const int hk = (4 * (lane + kWave * k) / D) % G;  // the row this float4 belongs to
+      acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int q = 0; q < NPF; ++q) {
+        const float fq = __shfl(f, q * G + hk);
+        if (fq != 0.f) {  // runs of pieces without weight (never written) are not used
+          acc[k].x += fq * x[q][k].x;
+          acc[k].y += fq * x[q][k].y;
+          acc[k].z += fq * x[q][k].z;
+          acc[k].w += fq * x[q][k].w;
+        }
+      }
+      const float d = __shfl(den, hk);
+      sc[k] = d > 0.f ? 1.f / d : 0.f;
+    }
+    if (lane < ACTIVE) {
+#pragma unroll
+      for (int k = 0; k < NF4; ++k)
+        *(float4*)(out + 4 * (lane + kWave * k)) =
+            make_float4(acc[k].x * sc[k], acc[k].y * sc[k], acc[k].z * sc[k], acc[k].w * sc[k]);
+    }
+    return;
+  }
   float M = kNegInf;
   for (int p0 = 0; p0 < np; p0 += PP)
     if (p0 + qw < np && live(p0 + qw)) M = fmaxf(M, a.ws_m[(slot0 + p0 + qw) * R + row0 + hw]);

@@ -240,9 +240,12 @@ static hipError_t launch_stream_d(const DecodeArgs& a, hipStream_t s, bool merge
 }
 
 // The same merge for segments of many pieces (a few long contexts): one workgroup per
-// output row, its four waves each taking a contiguous quarter of the pieces; the quarter
-// maxima, then the weighted sums, are combined through LDS.  Spreads the latency-bound
-// chain of loads over four waves when there are too few rows to fill the GPU.
+// output row, its four waves each taking a contiguous quarter of the pieces.  Spreads the
+// latency-bound chain of loads over four waves when there are too few rows to fill the GPU.
+// Up to kFastPieces pieces per wave: each wave requests its pieces' m, l and rows at once
+// and weighs them against its own maximum; the four (maximum, sum of weights, weighted row)
+// triples are then rescaled to the common maximum through LDS.  More pieces: the quarter
+// maxima first, then the weighted sums.
 template <int D>
 __global__ __launch_bounds__(kMergeWaves * kWave) void stream_merge_long_kernel(DecodeArgs a) {
   constexpr int PER = D / kWave;
@@ -269,6 +272,74 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void stream_merge_long_kernel(
     return T * cc / a.chunks != T * (cc + 1) / a.chunks;
   };
   const int lo = (int)((long long)np * w / kMergeWaves), hi = (int)((long long)np * (w + 1) / kMergeWaves);
+  if constexpr (D <= 128) {
+    constexpr int LPR = D / 4, RPW = kWave / LPR, U = kFastPieces / RPW;
+    if (np <= kMergeWaves * kFastPieces) {  // workgroup-uniform; hi - lo <= kFastPieces
+      const int n = hi - lo, sub = lane / LPR, col = lane % LPR;
+      float mp = kNegInf, lp = 0.f;
+      if (lane < n && live(lo + lane)) {
+        mp = a.ws_m[(slot0 + lo + lane) * G + h];
+        lp = a.ws_l[(slot0 + lo + lane) * G + h];
+      }
+      float4 x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = u * RPW + sub;
+        x[u] = j < n ? *(const float4*)(a.ws_o + ((slot0 + lo + j) * G + h) * D + 4 * col)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      float Mw = mp;
+#pragma unroll
+      for (int s = 32; s >= 1; s >>= 1) Mw = fmaxf(Mw, __shfl_xor(Mw, s));
+      const float f = (mp == kNegInf) ? 0.f : fast_exp2(mp - Mw);
+      float den = f * lp;
+#pragma unroll
+      for (int s = 32; s >= 1; s >>= 1) den += __shfl_xor(den, s);
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float fj = __shfl(f, u * RPW + sub);
+        if (fj != 0.f) {  // rows of pieces without weight (never written) are not used
+          acc.x += fj * x[u].x;
+          acc.y += fj * x[u].y;
+          acc.z += fj * x[u].z;
+          acc.w += fj * x[u].w;
+        }
+      }
+#pragma unroll
+      for (int m = LPR; m < kWave; m <<= 1) {
+        acc.x += __shfl_xor(acc.x, m);
+        acc.y += __shfl_xor(acc.y, m);
+        acc.z += __shfl_xor(acc.z, m);
+        acc.w += __shfl_xor(acc.w, m);
+      }
+      if (lane < LPR) *(float4*)(&s_acc[w][4 * lane]) = acc;
+      if (lane == 0) {
+        s_m[w] = Mw;
+        s_den[w] = den;
+      }
+      __syncthreads();
+      if (w == 0) {
+        const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+        float wk[kMergeWaves], d = 0.f;
+#pragma unroll
+        for (int k = 0; k < kMergeWaves; ++k) {
+          wk[k] = s_m[k] == kNegInf ? 0.f : fast_exp2(s_m[k] - M);
+          d += wk[k] * s_den[k];
+        }
+        const float sc = d > 0.f ? 1.f / d : 0.f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const int e = lane + kWave * i;
+          float v = 0.f;
+#pragma unroll
+          for (int k = 0; k < kMergeWaves; ++k) v += wk[k] * s_acc[k][e];
+          out[e] = v * sc;
+        }
+      }
+      return;
+    }
+  }
   float M = kNegInf;
   for (int p0 = lo; p0 < hi; p0 += kWave)
     if (p0 + lane < hi && live(p0 + lane)) M = fmaxf(M, a.ws_m[(slot0 + p0 + lane) * G + h]);
