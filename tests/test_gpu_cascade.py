@@ -2,7 +2,7 @@
 against the fp64 oracle, which attends over each sequence's whole block table (prefix
 blocks followed by the tail blocks): the cascade must give the plain result.
 
-Covered: the FP8 shared-prefix workload reduced and at full size (sampled), bf16, every
+Covered: the FP8 shared-prefix workload reduced and at full size (every row), bf16, every
 group size the kernels take (the prefix pass then packs 32 / G sequences per row group,
 including a ragged last group), head dim 64, no prefix at all, empty tails, and a prefix
 that is the whole context."""

@@ -3,8 +3,8 @@ speculative decoding) through the C-ABI against the fp64 oracle.
 
 Every row count the kernel specialises on (q_len * G up to 16, 32 and 64 query rows per
 KV head) is compared element by element on reduced workloads spanning many tiles and
-ragged tails; the full-size 70B-shaped verify batch, as benchmarked, on a sample of
-sequences.  Edge cases: contexts shorter than q_len (early query tokens see nothing and
+ragged tails; the full-size 70B-shaped verify batch, as benchmarked, on every output
+row.  Edge cases: contexts shorter than q_len (early query tokens see nothing and
 give zeros), empty sequences, one long sequence spread over many chunks, q_len = 1
 against the single-token oracle, and block-permutation invariance (bitwise)."""
 
