@@ -136,6 +136,37 @@ def test_multi_full_size():
     assert_close(got, oracle_multi(w), "bf16", f"verify4, all {w.B} sequences")
 
 
+def test_multi_weighted_ranges_do_not_depend_on_the_first_xcd():
+    """The verify batch is large enough for XCD-weighted ranges, where a workgroup reads
+    which XCD runs it.  The call is repeated after 1 to 7 extra one-workgroup launches of
+    other work (which move the XCD that takes workgroup 0): every output must equal the
+    first bit for bit, and the first matches the oracle on sampled sequences."""
+    torch = torch_cuda()
+    import paged_kv_cache_288_amd as pkv
+    w = make_workload("verify4")
+    q = bits_to_device(torch, w.q.reshape(w.B, w.q_len, w.Hq, w.d))
+    kp, vp = bits_to_device(torch, w.k_pool), bits_to_device(torch, w.v_pool)
+    bt = torch.from_numpy(w.block_table).to("cuda")
+    cl = torch.from_numpy(w.context_lens).to("cuda")
+    out = torch.empty((w.B, w.q_len, w.Hq, w.d_v), dtype=torch.float32, device="cuda")
+
+    def call():
+        pkv.paged_decode_attn_multi(out, q, kp, vp, bt, cl, w.scale, w.max_context_len)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    first = call()
+    x = torch.zeros(64, device="cuda")
+    for extra in range(1, 8):
+        for _ in range(extra):
+            x.add_(1.0)
+        got = call()
+        log(f"[multi] after {extra} extra launches: equal={np.array_equal(got, first)}")
+        assert np.array_equal(got.view(np.uint32), first.view(np.uint32)), extra
+    seqs = [0, 40]
+    assert_close(first[seqs], oracle_multi(w, seqs), "bf16", "verify4 sampled sequences")
+
+
 def test_multi_rejects_unsupported():
     torch = torch_cuda()
     import paged_kv_cache_288_amd as pkv
