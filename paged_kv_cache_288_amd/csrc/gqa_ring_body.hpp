@@ -34,6 +34,14 @@ constexpr int kRingMaxSeqs = 4096;
 // the 4-wave shape, whose heavy tiles stream from HBM: the 8-wave shape serves groups whose
 // tiles are light, where a shared prefix re-read from each XCD's own L2 sets the pace.
 constexpr int kRingWeightMinTiles = 128;
+// XCD weights (parts of the tiles per chunk on even : odd XCDs).  The single-token kernel
+// takes 17:15 (18:14 and 33:31 measured 2-6 us slower per 70B-shaped call); the multi-token
+// kernel, whose tiles carry more arithmetic per byte, 33:31 (17:15 and even ranges 1-2 us
+// slower per verify call, 18:14 too).
+template <bool MULTI>
+struct RingWeights {
+  static constexpr int E = MULTI ? 33 : 17, O = MULTI ? 31 : 15;
+};
 
 typedef __attribute__((ext_vector_type(4))) int i32x4_t;
 typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
@@ -212,10 +220,12 @@ __device__ __forceinline__ void ring_setup(const RingWalk& g, int bid, lds_u8_t*
   const int T_head = __builtin_amdgcn_readfirstlane(s_pre[B]);
   const long long T = (long long)g.Hkv * T_head;
   const int C = g.chunks;
-  const bool wtd = may_weight && xcd_weighted(T, C, kRingWeightMinTiles, kRingMaxChunkTiles);
+  using Wt = RingWeights<MULTI>;
+  const bool wtd =
+      may_weight && xcd_weighted<Wt::E, Wt::O>(T, C, kRingWeightMinTiles, kRingMaxChunkTiles);
   if (bid == 0) {
     for (int i = tid; i <= B; i += NT) g.ws_prefix[i] = s_pre[i];
-    write_segment_ranges_xcd(g.ws_seg, s_pre, B, g.Hkv, C, wtd, tid, NT);
+    write_segment_ranges_xcd<Wt::E, Wt::O>(g.ws_seg, s_pre, B, g.Hkv, C, wtd, tid, NT);
   }
 
   // ---- this wave's chunk and, per lane, kRingTilesPerLane tiles' offset, length, segment
@@ -228,7 +238,8 @@ __device__ __forceinline__ void ring_setup(const RingWalk& g, int bid, lds_u8_t*
   int eighth = bid & 7;
   if (wtd && g.xcd8) eighth ^= (xcd_id() ^ bid) & 1;
   const int ch = eighth * (C / 8) + (bid >> 3) * WPG + w;
-  const long long tb = xcd_chunk_start(ch, T, C, wtd), te = xcd_chunk_start(ch + 1, T, C, wtd);
+  const long long tb = xcd_chunk_start<Wt::E, Wt::O>(ch, T, C, wtd),
+                  te = xcd_chunk_start<Wt::E, Wt::O>(ch + 1, T, C, wtd);
   const int ntl = (int)min(te - tb, (long long)kRingMaxChunkTiles);
   t.ntl = ntl;
   t.ch = ch;

@@ -178,38 +178,43 @@ __device__ __forceinline__ void write_segment_ranges(int32_t* ws_seg, PRE pre, i
 // XCD (i + r) mod 8, r the same for the whole grid but set by the dispatches before it.  The
 // balanced kernels give wave w of workgroup i the chunk e * C/8 + (i / 8) * waves + w, with
 // e = i mod 8 (weighted: with its lowest bit matched to the parity of the XCD it runs on), so
-// each XCD owns C/8 consecutive chunks.  (The multi-token kernel, at 8 waves per CU and
-// about 74 tiles per chunk on the 70B-shaped verify batch, measured 2.6 % slower
-// weighted, and splits evenly.)  Weighted, the chunks of even XCDs take 17
-// parts of the tiles for the odd ones' 15: W(c) counts the parts of chunks 0 .. c-1, and
-// chunk c covers tiles [T W(c) / 16C, T W(c+1) / 16C).  Unweighted, W(c) = 16 c: the equal
-// split above.
-constexpr int kXcdWeightEven = 17, kXcdWeightOdd = 15;  // parts per chunk; sum 2 x 16
-
+// each XCD owns C/8 consecutive chunks.  (The register-tile multi-token kernel, at 8 waves
+// per CU and about 74 tiles per chunk on the 70B-shaped verify batch, measured 2.6 % slower
+// weighted, and splits evenly.)  Weighted WE:WO, the chunks of even XCDs take WE parts of
+// the tiles for the odd ones' WO, H = (WE + WO) / 2 parts on average: W(c) counts the parts
+// of chunks 0 .. c-1, and chunk c covers tiles [T W(c) / HC, T W(c+1) / HC).  Unweighted,
+// W(c) = H c: the equal split above.
+template <int WE, int WO>
 __device__ __forceinline__ long long xcd_chunk_start(int c, long long T, int C, bool wtd) {
+  static_assert(WE > WO && (WE + WO) % 2 == 0, "XCD weights");
+  constexpr int H = (WE + WO) / 2;
   if (!wtd) return T * c / C;
   const int E = C / 8, x = c / E, r = c - x * E;
-  const long long W = (long long)E * (kXcdWeightEven * ((x + 1) >> 1) + kXcdWeightOdd * (x >> 1)) +
-                      (long long)r * ((x & 1) ? kXcdWeightOdd : kXcdWeightEven);
-  return T * W / (16LL * C);
+  const long long W = (long long)E * (WE * ((x + 1) >> 1) + WO * (x >> 1)) +
+                      (long long)r * ((x & 1) ? WO : WE);
+  return T * W / ((long long)H * C);
 }
 // The chunk holding tile t (0 <= t < T): the last c with xcd_chunk_start(c) <= t.
+template <int WE, int WO>
 __device__ __forceinline__ int xcd_chunk_of(long long t, long long T, int C, bool wtd) {
+  constexpr int H = (WE + WO) / 2;
   if (!wtd) return chunk_of(t, T, C);
   const long long E = C / 8;
-  const long long ws = ((t + 1) * 16LL * C - 1) / T;  // largest W(c) that still starts <= t
-  const long long pair = ws / (32 * E), rem = ws - pair * 32 * E;
-  if (rem < kXcdWeightEven * E) return (int)(2 * pair * E + rem / kXcdWeightEven);
-  return (int)((2 * pair + 1) * E + (rem - kXcdWeightEven * E) / kXcdWeightOdd);
+  const long long ws = ((t + 1) * H * C - 1) / T;  // largest W(c) that still starts <= t
+  const long long pair = ws / (2 * H * E), rem = ws - pair * 2 * H * E;
+  if (rem < WE * E) return (int)(2 * pair * E + rem / WE);
+  return (int)((2 * pair + 1) * E + (rem - WE * E) / WO);
 }
 // Whether to weight: chunks hold at least min_tiles tiles on average (below that the
 // weighting was measured to cost more than it saved), and the heavier chunks, up to
-// T * 17 / 16C + 1 tiles, still fit a wave's max_tiles.
+// T * WE / HC + 1 tiles, still fit a wave's max_tiles.
+template <int WE, int WO>
 __device__ __forceinline__ bool xcd_weighted(long long T, int C, int min_tiles, int max_tiles) {
-  return T >= (long long)min_tiles * C && kXcdWeightEven * T <= 16LL * C * (max_tiles - 1);
+  constexpr int H = (WE + WO) / 2;
+  return T >= (long long)min_tiles * C && WE * T <= (long long)H * C * (max_tiles - 1);
 }
 // write_segment_ranges over the (possibly weighted) ranges.
-template <typename PRE>
+template <int WE, int WO, typename PRE>
 __device__ __forceinline__ void write_segment_ranges_xcd(int32_t* ws_seg, PRE pre, int B, int H,
                                                          int C, bool wtd, int tid, int nthreads) {
   const int T_head = pre[B];
@@ -220,8 +225,8 @@ __device__ __forceinline__ void write_segment_ranges_xcd(int32_t* ws_seg, PRE pr
     int c0 = 0, n = 0;
     if (nb > 0) {
       const long long first = (long long)g * T_head + pre[b];
-      c0 = xcd_chunk_of(first, T, C, wtd);
-      n = xcd_chunk_of(first + nb - 1, T, C, wtd) - c0 + 1;
+      c0 = xcd_chunk_of<WE, WO>(first, T, C, wtd);
+      n = xcd_chunk_of<WE, WO>(first + nb - 1, T, C, wtd) - c0 + 1;
     }
     ws_seg[2 * sg] = c0;
     ws_seg[2 * sg + 1] = n;

@@ -174,43 +174,46 @@ def test_balanced_mode_piece_slots(lens, Hkv, C):
         assert chunks == live   # the merge reads exactly these pieces
 
 
-def _xcd_chunk_start(c, T, C, wtd):
+def _xcd_chunk_start(c, T, C, wtd, we=17, wo=15):
     if not wtd:
         return T * c // C
+    h = (we + wo) // 2
     E = C // 8
     x, r = divmod(c, E)
-    W = E * (17 * ((x + 1) // 2) + 15 * (x // 2)) + r * (15 if x & 1 else 17)
-    return T * W // (16 * C)
+    W = E * (we * ((x + 1) // 2) + wo * (x // 2)) + r * (wo if x & 1 else we)
+    return T * W // (h * C)
 
 
-def _xcd_chunk_of(t, T, C, wtd):
+def _xcd_chunk_of(t, T, C, wtd, we=17, wo=15):
     if not wtd:
         return chunk_of(t, T, C)
+    h = (we + wo) // 2
     E = C // 8
-    ws = ((t + 1) * 16 * C - 1) // T
-    pair, rem = divmod(ws, 32 * E)
-    if rem < 17 * E:
-        return 2 * pair * E + rem // 17
-    return (2 * pair + 1) * E + (rem - 17 * E) // 15
+    ws = ((t + 1) * h * C - 1) // T
+    pair, rem = divmod(ws, 2 * h * E)
+    if rem < we * E:
+        return 2 * pair * E + rem // we
+    return (2 * pair + 1) * E + (rem - we * E) // wo
 
 
-def _xcd_weighted(T, C, min_tiles, max_tiles):
-    return T >= min_tiles * C and 17 * T <= 16 * C * (max_tiles - 1)
+def _xcd_weighted(T, C, min_tiles, max_tiles, we=17, wo=15):
+    return T >= min_tiles * C and we * T <= (we + wo) // 2 * C * (max_tiles - 1)
 
 
+@pytest.mark.parametrize("we,wo", [(17, 15), (33, 31)])
 @pytest.mark.parametrize("T,C", [(128 * 64, 64), (70001, 64), (262144, 1024), (480 * 1024, 1024),
                                  (159952, 1024), (99991, 512), (152000, 2048), (2048 * 119, 2048)])
-def test_xcd_weighted_chunks(T, C):
-    """Host mirror of the balanced kernels' XCD-weighted ranges: they tile [0, T) in order,
-    the inverse used for the merge's bookkeeping names the range that holds each tile,
-    chunks of even XCDs hold about 17/15 of the odd ones' tiles, and whenever the weighting
-    is switched on (512 tiles per wave, chunk counts for 480) no range exceeds what a wave's
-    tables hold."""
+def test_xcd_weighted_chunks(T, C, we, wo):
+    """Host mirror of the balanced kernels' XCD-weighted ranges (17:15 for the single-token
+    ring kernel, 33:31 for the multi-token one): they tile [0, T) in order, the inverse used
+    for the merge's bookkeeping names the range that holds each tile, chunks of even XCDs
+    hold about we/wo of the odd ones' tiles, and whenever the weighting is switched on (512
+    tiles per wave, chunk counts for 480) no range exceeds what a wave's tables hold."""
     for max_tiles in (512, 128):
-        if _xcd_weighted(T, C, 64, max_tiles):
-            starts = [_xcd_chunk_start(c, T, C, True) for c in range(C + 1)]
+        if _xcd_weighted(T, C, 64, max_tiles, we, wo):
+            starts = [_xcd_chunk_start(c, T, C, True, we, wo) for c in range(C + 1)]
             assert max(b - a for a, b in zip(starts, starts[1:])) <= max_tiles
-    starts = [_xcd_chunk_start(c, T, C, True) for c in range(C + 1)]
+    starts = [_xcd_chunk_start(c, T, C, True, we, wo) for c in range(C + 1)]
     assert starts[0] == 0 and starts[-1] == T
     assert all(b > a for a, b in zip(starts, starts[1:]))   # every chunk non-empty
     if T <= 480 * C:   # the chunk count keeps T within this bound
@@ -218,10 +221,10 @@ def test_xcd_weighted_chunks(T, C):
     E = C // 8
     size = [starts[c + 1] - starts[c] for c in range(C)]
     even = sum(size[c] for c in range(C) if (c // E) % 2 == 0)
-    assert abs(even / (T - even) - 17 / 15) < 0.01
+    assert abs(even / (T - even) - we / wo) < 0.01
     step = max(1, T // 20000)
     for t in list(range(0, T, step)) + [s for s in starts[1:-1]] + [s - 1 for s in starts[1:]]:
-        c = _xcd_chunk_of(t, T, C, True)
+        c = _xcd_chunk_of(t, T, C, True, we, wo)
         assert starts[c] <= t < starts[c + 1], (t, c)
 
 
