@@ -13,9 +13,9 @@
 //
 // Compared with fixed partitions this keeps every wave streaming for the whole kernel with
 // the same amount of work (+-1 tile), without per-partition start-up, barriers or a ragged
-// last round.  Chunks are numbered so that each XCD (workgroup id mod 8 under round-robin
-// dispatch) gets a contiguous eighth of the space - one KV head when Hkv = 8 - so a shared
-// prefix's re-reads stay in that XCD's L2.
+// last round.  Chunks are numbered so that each XCD (workgroups go to the 8 XCDs in turn, so
+// those with equal ids mod 8 share one) gets a contiguous eighth of the space - one KV head
+// when Hkv = 8 - so a shared prefix's re-reads stay in that XCD's L2.
 #include "gqa_ring_body.hpp"
 #include "gqa_stream_body.hpp"
 

@@ -40,8 +40,8 @@ constexpr int kMaxPartitionTokens = 4096;  // 64 tiles of 16 tokens per wave, 4 
 constexpr int kMaxStreamSeqs = 4096;       // balanced mode: sequences per call
 constexpr long long kMaxChunkTiles = 128;  // balanced mode: tiles per wave
 constexpr int kRingMaxWavesPerCu = 8;      // the default decode kernel: 4 or 8 waves per CU
-// and about 480 tiles per wave, so that a chunk weighted 17/16 by XCD still fits the 512
-// tiles a wave's tables hold
+// and about 480 tiles per wave, so that a chunk weighted 17/16 (single-token) or 33/32
+// (multi-token) by XCD still fits the 512 tiles a wave's tables hold
 constexpr long long kRingChunkTiles = 480;
 
 int32_t ring_chunks(int32_t B, int32_t Hkv, int32_t max_ctx, int waves_per_cu);
