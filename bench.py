@@ -44,6 +44,8 @@ KERNEL_SOURCES = {
     "gqa": ["paged_kv_cache_288_amd/csrc/gqa_stream.hip", "paged_kv_cache_288_amd/csrc/gqa_ring_body.hpp",
             "paged_kv_cache_288_amd/csrc/gqa_stream_body.hpp",
             "paged_kv_cache_288_amd/csrc/gqa_decode.hip", "paged_kv_cache_288_amd/csrc/gqa_tile.hpp",
+            "paged_kv_cache_288_amd/csrc/gqa_multi.hip", "paged_kv_cache_288_amd/csrc/gqa_multi_ring_body.hpp",
+            "paged_kv_cache_288_amd/csrc/gqa_multi_body.hpp",
             "paged_kv_cache_288_amd/csrc/pkv_device.hpp"],
     "mla": ["paged_kv_cache_288_amd/csrc/mla_stream.hip", "paged_kv_cache_288_amd/csrc/gqa_stream.hip",
             "paged_kv_cache_288_amd/csrc/gqa_stream_body.hpp", "paged_kv_cache_288_amd/csrc/gqa_tile.hpp",
@@ -133,6 +135,9 @@ def kernel_label(w, pkv, ps, cascade=False):
             return "pkv_paged_decode_attn_mla call, balanced mode (mla_stream_kernel + stream_merge_kernel<512>)"
         return "pkv_paged_decode_attn_mla call, partitioned (mla_decode_kernel + partition_merge_kernel<512>)"
     if pkv.decode_partition_size(w.B, w.Hkv, w.max_context_len, ps) == 0:
+        if w.kv_dtype == "bf16" and w.d == 128:
+            return ("pkv_paged_decode_attn call, balanced mode (gqa_multi_ring_kernel<1>, one query "
+                    "row per sequence, + stream_merge_kernel)")
         return "pkv_paged_decode_attn call, balanced mode (gqa_ring_kernel + stream_merge_kernel)"
     return "pkv_paged_decode_attn call, partitioned (gqa_decode_kernel + partition_merge_kernel)"
 

@@ -266,6 +266,17 @@ int multi_waves_per_cu(int d, int rows) {
   return kMW * multi_waves_per_simd(64, rt);
 }
 
+hipError_t launch_gqa_multi_ring_pieces(const MultiArgs& a, hipStream_t s) {
+  const int R = a.Hq / a.Hkv * a.q_len;
+  if (a.d != 128 || a.fp8 || R > 32 || a.chunks % (8 * kRingWaves) || a.B > kRingMaxSeqs ||
+      a.block_size % kTile || a.q_rows != a.B * a.q_len || a.fixed_len >= 0)
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(a.chunks / kRingWaves)), block(kRingWaves * kWave);
+  if (R <= 16) hipLaunchKernelGGL((gqa_multi_ring_kernel<1>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((gqa_multi_ring_kernel<2>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_gqa_multi(const MultiArgs& a, hipStream_t s) {
   if (a.B > kMultiSeqs || a.chunks % 32 || a.block_size % kTile) return hipErrorInvalidValue;
   if (a.d == 128) return a.fp8 ? launch_multi_d<128, true>(a, s) : launch_multi_d<128, false>(a, s);

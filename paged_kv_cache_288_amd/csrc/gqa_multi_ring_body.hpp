@@ -59,7 +59,8 @@ __device__ __forceinline__ void gqa_multi_ring_body(const MultiArgs& a, int bid,
                     min(a.max_blocks * a.block_size, a.max_len), a.chunks, a.ws_prefix, a.ws_seg,
                     a.xcd8};
   RingTiles tl;
-  ring_setup<M::ROW, WPG, true>(gw, bid, lds, true, tl);  // XCD-weighted ranges for large calls
+  // XCD-weighted ranges for large calls
+  ring_setup<M::ROW, WPG, true, RingWeights<RT>>(gw, bid, lds, true, tl);
   const int ntl = tl.ntl, ch = tl.ch;
   if (ntl <= 0) return;
   uint32_t (&off_l)[kRingTilesPerLane] = tl.off;

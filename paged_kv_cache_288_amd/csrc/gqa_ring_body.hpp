@@ -34,13 +34,16 @@ constexpr int kRingMaxSeqs = 4096;
 // the 4-wave shape, whose heavy tiles stream from HBM: the 8-wave shape serves groups whose
 // tiles are light, where a shared prefix re-read from each XCD's own L2 sets the pace.
 constexpr int kRingWeightMinTiles = 128;
-// XCD weights (parts of the tiles per chunk on even : odd XCDs).  The single-token kernel
-// takes 17:15 (18:14 and 33:31 measured 2-6 us slower per 70B-shaped call); the multi-token
-// kernel, whose tiles carry more arithmetic per byte, 33:31 (17:15 and even ranges 1-2 us
-// slower per verify call, 18:14 too).
-template <bool MULTI>
+// XCD weights (parts of the tiles per chunk on even : odd XCDs) by kernel, RT its MFMA row
+// tiles (0: the VALU ring).  Single-token calls, on the VALU ring or on the MFMA ring with
+// one 16-row tile, take 17:15 (on the 70B-shaped batch 18:14 and 33:31 measured 2-6 us
+// slower per call with the VALU ring, and 33:31 about 1.3 us slower with the MFMA ring);
+// the MFMA ring with two row tiles (32 query rows: the verify pass), whose tiles carry more
+// arithmetic per byte, 33:31 (17:15 and even ranges 1-2 us slower per verify call, 18:14
+// too).
+template <int RT>
 struct RingWeights {
-  static constexpr int E = MULTI ? 33 : 17, O = MULTI ? 31 : 15;
+  static constexpr int E = RT >= 2 ? 33 : 17, O = RT >= 2 ? 31 : 15;
 };
 
 typedef __attribute__((ext_vector_type(4))) int i32x4_t;
@@ -173,7 +176,7 @@ struct RingTiles {
 // when `may_weight` and the call is large), and the tables.  ROW = bytes per K or V row;
 // MULTI: also the lengths and the first tile's index (RingTiles::len, tt_first), and lengths
 // from fixed_len when context_lens is null (the single-token kernel needs none of these).
-template <int ROW, int WPG, bool MULTI>
+template <int ROW, int WPG, bool MULTI, typename Wt>
 __device__ __forceinline__ void ring_setup(const RingWalk& g, int bid, lds_u8_t* lds,
                                            bool may_weight, RingTiles& t) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -220,7 +223,6 @@ __device__ __forceinline__ void ring_setup(const RingWalk& g, int bid, lds_u8_t*
   const int T_head = __builtin_amdgcn_readfirstlane(s_pre[B]);
   const long long T = (long long)g.Hkv * T_head;
   const int C = g.chunks;
-  using Wt = RingWeights<MULTI>;
   const bool wtd =
       may_weight && xcd_weighted<Wt::E, Wt::O>(T, C, kRingWeightMinTiles, kRingMaxChunkTiles);
   if (bid == 0) {
@@ -336,7 +338,7 @@ __device__ __forceinline__ void gqa_ring_body(const DecodeArgs& a, int bid, lds_
                     a.num_blocks, min(a.max_blocks * a.block_size, a.max_context_len), a.chunks,
                     a.ws_prefix, a.ws_seg, a.xcd8};
   RingTiles tl;
-  ring_setup<Lo::ROW, WPG, false>(gw, bid, lds, WPG == 4, tl);
+  ring_setup<Lo::ROW, WPG, false, RingWeights<0>>(gw, bid, lds, WPG == 4, tl);
   const int ntl = tl.ntl, ch = tl.ch;
   if (ntl <= 0) return;
   uint32_t (&off_l)[kRingTilesPerLane] = tl.off;

@@ -359,7 +359,12 @@ pkv_status pkv_paged_decode_attn(float* out, const void* q, const void* k_pool,
   if (ps < 0) return PKV_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
   if (ps == 0) {  // balanced mode
-    const int32_t chunks = ring_chunks(B, Hkv, ctx, pkv::ring_waves_per_cu(d, G, fp8));
+    // bf16 K/V with 128 dims: the LDS ring on MFMA (each sequence's G query rows in one
+    // 16-row tile of the multi-token ring kernel, q_len = 1); otherwise the VALU ring
+    const bool mfma = d == 128 && !fp8;
+    const int32_t chunks = ring_chunks(B, Hkv, ctx,
+                                       mfma ? pkv::multi_ring_waves_per_cu()
+                                            : pkv::ring_waves_per_cu(d, G, fp8));
     if (chunks < 0) return PKV_ERR_SHAPE;
     const size_t need = stream_ws_bytes(B, Hq, Hkv, d, chunks);
     if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
@@ -376,7 +381,22 @@ pkv_status pkv_paged_decode_attn(float* out, const void* q, const void* k_pool,
                       k_scale, v_scale, block_table, context_lens, ws_m, ws_l, ws_o,
                       B, Hq, Hkv, d, block_size, num_blocks, max_blocks_per_seq, ctx,
                       0, 0, scale, fp8 ? 1 : 0, chunks, ws_p, ws_s, device_xcd8() ? 1 : 0};
-    return hip_status(pkv::launch_gqa_stream(a, s));
+    if (!mfma) return hip_status(pkv::launch_gqa_stream(a, s));
+    pkv::MultiArgs m{};
+    m.out = nullptr;
+    m.q = (const uint16_t*)q;
+    m.k_pool = (const uint8_t*)k_pool;
+    m.v_pool = (const uint8_t*)v_pool;
+    m.block_table = block_table;
+    m.context_lens = context_lens;
+    m.ws_m = ws_m, m.ws_l = ws_l, m.ws_o = ws_o, m.ws_prefix = ws_p, m.ws_seg = ws_s;
+    m.B = B, m.q_len = 1, m.Hq = Hq, m.Hkv = Hkv, m.d = d, m.block_size = block_size;
+    m.num_blocks = num_blocks, m.max_blocks = max_blocks_per_seq, m.max_len = ctx;
+    m.table_stride = max_blocks_per_seq, m.fixed_len = -1, m.q_rows = B;
+    m.causal = 1, m.fp8 = 0, m.scale = scale, m.chunks = chunks, m.xcd8 = a.xcd8;
+    const pkv_status st = hip_status(pkv::launch_gqa_multi_ring_pieces(m, s));
+    if (st != PKV_OK) return st;
+    return hip_status(pkv::launch_stream_merge(a, s));
   }
   const int32_t P = num_parts(ctx, ps);
   if (P > kGridYZMax) return PKV_ERR_SHAPE;

@@ -204,8 +204,8 @@ def _xcd_weighted(T, C, min_tiles, max_tiles, we=17, wo=15):
 @pytest.mark.parametrize("T,C", [(128 * 64, 64), (70001, 64), (262144, 1024), (480 * 1024, 1024),
                                  (159952, 1024), (99991, 512), (152000, 2048), (2048 * 119, 2048)])
 def test_xcd_weighted_chunks(T, C, we, wo):
-    """Host mirror of the balanced kernels' XCD-weighted ranges (17:15 for the single-token
-    ring kernel, 33:31 for the multi-token one): they tile [0, T) in order, the inverse used
+    """Host mirror of the balanced kernels' XCD-weighted ranges (17:15 for single-token
+    calls, 33:31 for the 32-row tiles of the verify pass): they tile [0, T) in order, the inverse used
     for the merge's bookkeeping names the range that holds each tile, chunks of even XCDs
     hold about we/wo of the odd ones' tiles, and whenever the weighting is switched on (512
     tiles per wave, chunk counts for 480) no range exceeds what a wave's tables hold."""
