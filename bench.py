@@ -135,10 +135,12 @@ def kernel_label(w, pkv, ps, cascade=False):
             return "pkv_paged_decode_attn_mla call, balanced mode (mla_stream_kernel + stream_merge_kernel<512>)"
         return "pkv_paged_decode_attn_mla call, partitioned (mla_decode_kernel + partition_merge_kernel<512>)"
     if pkv.decode_partition_size(w.B, w.Hkv, w.max_context_len, ps) == 0:
+        # the merge: stream_merge_long_kernel when segments average more than 16 pieces
+        merge = "stream_merge_kernel / stream_merge_long_kernel"
         if w.kv_dtype == "bf16" and w.d == 128:
             return ("pkv_paged_decode_attn call, balanced mode (gqa_multi_ring_kernel<1>, one query "
-                    "row per sequence, + stream_merge_kernel)")
-        return "pkv_paged_decode_attn call, balanced mode (gqa_ring_kernel + stream_merge_kernel)"
+                    "row per sequence, + %s)" % merge)
+        return "pkv_paged_decode_attn call, balanced mode (gqa_ring_kernel + %s)" % merge
     return "pkv_paged_decode_attn call, partitioned (gqa_decode_kernel + partition_merge_kernel)"
 
 
