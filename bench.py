@@ -140,6 +140,9 @@ def kernel_label(w, pkv, ps, cascade=False):
         if w.kv_dtype == "bf16" and w.d == 128:
             return ("pkv_paged_decode_attn call, balanced mode (gqa_multi_ring_kernel<1>, one query "
                     "row per sequence, + %s)" % merge)
+        if w.d == 128:
+            return ("pkv_paged_decode_attn call, balanced mode (gqa_multi_kernel<128, 1, true>, one "
+                    "query row per sequence, + %s)" % merge)
         return "pkv_paged_decode_attn call, balanced mode (gqa_ring_kernel + %s)" % merge
     return "pkv_paged_decode_attn call, partitioned (gqa_decode_kernel + partition_merge_kernel)"
 

@@ -220,8 +220,10 @@ __global__ __launch_bounds__(kMultiMergeWaves * kWave) void multi_merge_kernel(M
   }
 }
 
+// The decode kernel alone: the LDS ring on MFMA for bf16 with d = 128 and up to 32 rows,
+// else the register-tile kernel.
 template <int D, int RT, bool FP8>
-static hipError_t launch_multi_one(const MultiArgs& a, hipStream_t s) {
+static hipError_t launch_multi_decode(const MultiArgs& a, hipStream_t s) {
   const int R = a.Hq / a.Hkv * a.q_len;
   if (multi_uses_ring(D, R, FP8)) {  // chunks were sized for it (up to 480 tiles each)
     if constexpr (D == 128 && RT <= 2 && !FP8) {
@@ -237,8 +239,13 @@ static hipError_t launch_multi_one(const MultiArgs& a, hipStream_t s) {
   } else {
     hipLaunchKernelGGL((gqa_multi_kernel<D, RT, FP8>), dim3(a.chunks / kMW), dim3(kMW * kWave), 0, s, a);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+template <int D, int RT, bool FP8>
+static hipError_t launch_multi_one(const MultiArgs& a, hipStream_t s, bool merge) {
+  hipError_t e = launch_multi_decode<D, RT, FP8>(a, s);
+  if (e != hipSuccess || !merge) return e;
   const dim3 grid((unsigned)(((long long)a.B * a.q_len * a.Hkv + kMultiMergeWaves - 1) / kMultiMergeWaves));
   const dim3 block(kMultiMergeWaves * kWave);
   switch (a.Hq / a.Hkv) {
@@ -252,11 +259,20 @@ static hipError_t launch_multi_one(const MultiArgs& a, hipStream_t s) {
 }
 
 template <int D, bool FP8>
-static hipError_t launch_multi_d(const MultiArgs& a, hipStream_t s) {
+static hipError_t launch_multi_d(const MultiArgs& a, hipStream_t s, bool merge) {
   const int R = a.Hq / a.Hkv * a.q_len;
-  if (R <= 16) return launch_multi_one<D, 1, FP8>(a, s);
-  if (R <= 32) return launch_multi_one<D, 2, FP8>(a, s);
-  if (R <= 64) return launch_multi_one<D, 4, FP8>(a, s);
+  if (R <= 16) return launch_multi_one<D, 1, FP8>(a, s, merge);
+  if (R <= 32) return launch_multi_one<D, 2, FP8>(a, s, merge);
+  if (R <= 64) return launch_multi_one<D, 4, FP8>(a, s, merge);
+  return hipErrorInvalidValue;
+}
+
+static hipError_t launch_multi_impl(const MultiArgs& a, hipStream_t s, bool merge) {
+  if (a.B > kMultiSeqs || a.chunks % 32 || a.block_size % kTile) return hipErrorInvalidValue;
+  if (a.d == 128)
+    return a.fp8 ? launch_multi_d<128, true>(a, s, merge) : launch_multi_d<128, false>(a, s, merge);
+  if (a.d == 64)
+    return a.fp8 ? launch_multi_d<64, true>(a, s, merge) : launch_multi_d<64, false>(a, s, merge);
   return hipErrorInvalidValue;
 }
 
@@ -266,25 +282,12 @@ int multi_waves_per_cu(int d, int rows) {
   return kMW * multi_waves_per_simd(64, rt);
 }
 
-hipError_t launch_gqa_multi_ring_pieces(const MultiArgs& a, hipStream_t s) {
-  const int R = a.Hq / a.Hkv * a.q_len;
-  if (a.d != 128 || a.fp8 || R > 32 || a.chunks % (8 * kRingWaves) || a.B > kRingMaxSeqs ||
-      a.block_size % kTile || a.q_rows != a.B * a.q_len || a.fixed_len >= 0)
-    return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(a.chunks / kRingWaves)), block(kRingWaves * kWave);
-  if (R <= 16) hipLaunchKernelGGL((gqa_multi_ring_kernel<1>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((gqa_multi_ring_kernel<2>), grid, block, 0, s, a);
-  return hipGetLastError();
+hipError_t launch_gqa_multi_pieces(const MultiArgs& a, hipStream_t s) {
+  return launch_multi_impl(a, s, false);
 }
 
 hipError_t launch_gqa_multi(const MultiArgs& a, hipStream_t s) {
-  if (a.B > kMultiSeqs || a.chunks % 32 || a.block_size % kTile) return hipErrorInvalidValue;
-  if (a.d == 128) return a.fp8 ? launch_multi_d<128, true>(a, s) : launch_multi_d<128, false>(a, s);
-  if (a.d == 64) return a.fp8 ? launch_multi_d<64, true>(a, s) : launch_multi_d<64, false>(a, s);
-  return hipErrorInvalidValue;
+  return launch_multi_impl(a, s, true);
 }
-
-
-
 
 }  // namespace pkv

@@ -320,7 +320,13 @@ size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d_
   const int32_t ps = pkv_decode_partition_size(B, Hkv, max_context_len, partition_size);
   if (ps < 0 || Hq <= 0 || d_v <= 0 || Hq % Hkv) return 0;
   if (ps == 0) {
-    const int32_t chunks = ring_chunks(B, Hkv, max_context_len, kRingMaxWavesPerCu);
+    // the most chunks any balanced kernel of the call can take: the VALU ring at 8 waves per
+    // CU, or for d = 128 (FP8 K/V: the register-tile MFMA kernel) up to 128 tiles per chunk
+    int32_t chunks = ring_chunks(B, Hkv, max_context_len, kRingMaxWavesPerCu);
+    if (d_v == 128 && chunks >= 0) {
+      const int32_t tile_chunks = multi_chunks(B, 1, Hq, Hkv, d_v, max_context_len, false);
+      chunks = tile_chunks < 0 ? -1 : (tile_chunks > chunks ? tile_chunks : chunks);
+    }
     return chunks < 0 ? 0 : stream_ws_bytes(B, Hq, Hkv, d_v, chunks);
   }
   return ws_bytes(B, Hq, d_v, num_parts(max_context_len, ps));
@@ -359,12 +365,12 @@ pkv_status pkv_paged_decode_attn(float* out, const void* q, const void* k_pool,
   if (ps < 0) return PKV_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
   if (ps == 0) {  // balanced mode
-    // bf16 K/V with 128 dims: the LDS ring on MFMA (each sequence's G query rows in one
-    // 16-row tile of the multi-token ring kernel, q_len = 1); otherwise the VALU ring
-    const bool mfma = d == 128 && !fp8;
-    const int32_t chunks = ring_chunks(B, Hkv, ctx,
-                                       mfma ? pkv::multi_ring_waves_per_cu()
-                                            : pkv::ring_waves_per_cu(d, G, fp8));
+    // d = 128: the multi-token kernels with q_len = 1 (each sequence's G query rows in one
+    // 16-row MFMA tile): for bf16 K/V the LDS ring, for FP8 the register-tile kernel; d = 64:
+    // the VALU ring
+    const bool mfma = d == 128;
+    const int32_t chunks = mfma ? multi_chunks(B, 1, Hq, Hkv, d, ctx, !fp8)
+                                : ring_chunks(B, Hkv, ctx, pkv::ring_waves_per_cu(d, G, fp8));
     if (chunks < 0) return PKV_ERR_SHAPE;
     const size_t need = stream_ws_bytes(B, Hq, Hkv, d, chunks);
     if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
@@ -387,14 +393,16 @@ pkv_status pkv_paged_decode_attn(float* out, const void* q, const void* k_pool,
     m.q = (const uint16_t*)q;
     m.k_pool = (const uint8_t*)k_pool;
     m.v_pool = (const uint8_t*)v_pool;
+    m.k_scale = k_scale;
+    m.v_scale = v_scale;
     m.block_table = block_table;
     m.context_lens = context_lens;
     m.ws_m = ws_m, m.ws_l = ws_l, m.ws_o = ws_o, m.ws_prefix = ws_p, m.ws_seg = ws_s;
     m.B = B, m.q_len = 1, m.Hq = Hq, m.Hkv = Hkv, m.d = d, m.block_size = block_size;
     m.num_blocks = num_blocks, m.max_blocks = max_blocks_per_seq, m.max_len = ctx;
     m.table_stride = max_blocks_per_seq, m.fixed_len = -1, m.q_rows = B;
-    m.causal = 1, m.fp8 = 0, m.scale = scale, m.chunks = chunks, m.xcd8 = a.xcd8;
-    const pkv_status st = hip_status(pkv::launch_gqa_multi_ring_pieces(m, s));
+    m.causal = 1, m.fp8 = fp8 ? 1 : 0, m.scale = scale, m.chunks = chunks, m.xcd8 = a.xcd8;
+    const pkv_status st = hip_status(pkv::launch_gqa_multi_pieces(m, s));
     if (st != PKV_OK) return st;
     return hip_status(pkv::launch_stream_merge(a, s));
   }

@@ -152,10 +152,10 @@ struct MultiArgs {
 };
 // Decode kernel + merge kernel.
 hipError_t launch_gqa_multi(const MultiArgs& a, hipStream_t s);
-// The LDS-ring decode kernel on MFMA only (bf16, d = 128, q_len * G <= 32 rows), leaving its
-// pieces (rows of q_len * G per slot) for a later merge.  With q_len = 1 they are laid out
-// as the single-token balanced kernel's, so launch_stream_merge combines them.
-hipError_t launch_gqa_multi_ring_pieces(const MultiArgs& a, hipStream_t s);
+// The decode kernel only (the ring or the register-tile kernel, as launch_gqa_multi picks),
+// leaving its pieces (rows of q_len * G per slot) for a later merge.  With q_len = 1 they
+// are laid out as the single-token balanced kernel's, so launch_stream_merge combines them.
+hipError_t launch_gqa_multi_pieces(const MultiArgs& a, hipStream_t s);
 // Resident waves per CU of the multi-token decode kernel for head dim d and q_len * G rows.
 int multi_waves_per_cu(int d, int rows);
 // Whether the multi-token call runs the LDS-ring kernel (then multi_ring_waves_per_cu()

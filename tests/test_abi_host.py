@@ -132,6 +132,10 @@ def test_balanced_mode_workspace_size(lib):
     for B, Hq, Hkv, d, ctx in [(64, 64, 8, 128, 8192), (2, 4, 1, 64, 256), (4, 64, 8, 128, 32768),
                                (1, 8, 1, 128, 0), (3, 12, 3, 64, 700)]:
         C = _stream_chunks(B, Hkv, ctx, 256)
+        if d == 128:  # FP8 calls run the register-tile MFMA kernel: up to 128 tiles per chunk
+            tmax = Hkv * B * ((ctx + 15) // 16)
+            c = max(min(8 * 256, tmax), -(-tmax // 128))
+            C = max(C, max(32, -(-c // 32) * 32))
         rows = (C + Hkv * B) * (Hq // Hkv)
         want = 2 * r256(rows * 4) + r256(rows * d * 4) + r256((B + 1) * 4) + r256(Hkv * B * 8)
         assert lib.pkv_decode_workspace_bytes(B, Hq, Hkv, d, ctx, 0) == want
